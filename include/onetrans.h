@@ -1,0 +1,203 @@
+/*
+ * onetrans.h - C ABI of the OneTrans block-stack forward pass on MI355X (gfx950).
+ *
+ * The method (agihunt.info summary of OneTrans, arXiv 2510.26104, "method"
+ * paragraphs; asterzephyr.xyz blog, designs two to four):
+ *   - one token sequence per (user, candidate): S-tokens (behaviour history)
+ *     first, then n_ns NS-tokens (user / item / context fields);
+ *   - every block is a pre-norm (RMSNorm) causal Transformer layer with mixed
+ *     parameters: all S-tokens share one QKV projection and one FFN, NS position
+ *     k has its own private QKV projection and FFN;
+ *   - an S-token sees earlier events and itself; an NS-token sees every present
+ *     S-token and the NS-tokens up to itself;
+ *   - pyramid: layer l keeps only the last q_l S rows as queries, while its keys
+ *     and values cover all S rows that enter the layer;
+ *   - the S side never sees NS tokens, so its per-layer K/V is computed once per
+ *     user, cached, extended by newly arrived events, and shared by every
+ *     candidate; only the NS side runs per candidate.
+ * Readings where the pages are silent: no biases; no output projection (heads
+ * are concatenated into the residual); score scale 1/sqrt(head_dim); RMSNorm
+ * x / sqrt(mean(x^2) + eps) * g; FFN = W2 GELU_erf(W1 x) with a residual; no
+ * positional term inside the block; an appended event is a query at every layer.
+ *
+ * Conventions for every call:
+ *   - Device memory is owned by the caller (for instance torch tensors). The
+ *     library allocates no device memory and keeps no pointer after a call
+ *     returns. "dev" marks device pointers, "host" host pointers.
+ *   - Compute calls are asynchronous on `stream` (NULL = the default stream).
+ *     They validate every argument on the host first and return a status with
+ *     no side effect when something is wrong. A launch failure returns
+ *     ONETRANS_ERR_HIP; faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Matrices use the torch Linear layout [out][in]; all arrays are dense,
+ *     row-major and 16-byte aligned.
+ *   - Numerics: RMSNorm, softmax and the residual stream in fp32; the five
+ *     linear maps take fp16 operands (bf16 weights converted exactly at pack
+ *     time, E4M3FN weights decoded exactly) with fp32 accumulation; attention
+ *     takes bf16 Q, K, V and probabilities with fp32 accumulation.
+ *   - Not thread-safe for concurrent calls that share a workspace or a cache;
+ *     calls on distinct workspaces and caches are independent.
+ *   - onetrans_last_error() returns a thread-local description of the last
+ *     failure of the calling thread.
+ */
+#ifndef ONETRANS_H
+#define ONETRANS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ONETRANS_MAX_LAYERS 16
+
+typedef enum {
+  ONETRANS_OK = 0,
+  ONETRANS_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, misaligned pointer */
+  ONETRANS_ERR_UNSUPPORTED = 2,   /* shape outside the supported set (see onetrans_config) */
+  ONETRANS_ERR_WORKSPACE = 3,     /* workspace or buffer smaller than the sizing call asks */
+  ONETRANS_ERR_CAPACITY = 4,      /* append beyond the cache's append capacity */
+  ONETRANS_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+} onetrans_status;
+
+typedef enum { ONETRANS_W_BF16 = 0, ONETRANS_W_FP8_E4M3 = 1 } onetrans_wdtype;
+
+/* Model shape. Supported: 1 <= n_layers <= 16; d_model % 64 == 0 and
+ * d_model <= 1024; head_dim = d_model / n_heads in {32, 64}; ffn_hidden % 64 == 0;
+ * 1 <= n_ns <= 256; s_len >= 1; q_sched[0] <= s_len and
+ * q_sched[l] <= q_sched[l-1], every q_sched[l] >= 1 (pyramid: layer l keeps
+ * the last q_sched[l] S rows; layer l's input has n_l = s_len (l = 0) or
+ * q_sched[l-1] rows); append_cap >= 0 (events a cache can take after its
+ * prefill); rms_eps > 0; ns_wdtype one of onetrans_wdtype (S weights are always
+ * bf16). */
+typedef struct onetrans_config {
+  int32_t n_layers, d_model, n_heads, ffn_hidden, n_ns, s_len;
+  int32_t q_sched[ONETRANS_MAX_LAYERS];
+  int32_t append_cap;
+  float rms_eps;
+  int32_t ns_wdtype;
+} onetrans_config;
+
+/* One layer's parameters as the caller holds them (dev pointers, read only).
+ *   s_wqkv  bf16 [3d][d]   rows 0..d-1 = W_Q, d..2d-1 = W_K, 2d..3d-1 = W_V
+ *   s_w1    bf16 [F][d]    s_w2 bf16 [d][F]
+ *   s_g_attn, s_g_ffn  fp32 [d]       RMSNorm gains of the S rows
+ *   ns_wqkv bf16|e4m3 [n_ns][3d][d]   ns_w1 [n_ns][F][d]   ns_w2 [n_ns][d][F]
+ *   ns_scale fp32 [n_ns][5]  per-matrix scale (W_Q, W_K, W_V, W1, W2) when the
+ *            NS weights are E4M3FN codes (effective weight = scale * code); NULL for bf16
+ *   ns_g_attn, ns_g_ffn fp32 [n_ns][d]  RMSNorm gains of NS position k */
+typedef struct onetrans_layer_weights {
+  const void *s_wqkv, *s_w1, *s_w2;
+  const float *s_g_attn, *s_g_ffn;
+  const void *ns_wqkv, *ns_w1, *ns_w2;
+  const float *ns_scale;
+  const float *ns_g_attn, *ns_g_ffn;
+} onetrans_layer_weights;
+
+/* A per-user, per-layer S-side K/V cache living in one caller-owned device
+ * buffer (layout private to the library; it is plain device memory, so it can
+ * be copied, saved and restored byte for byte together with this struct).
+ * Layer l holds n_l + append_cap rows per user; rows [0, n_l + n_appended) are
+ * filled. Fields are set by onetrans_kv_cache_init and updated by the calls. */
+typedef struct onetrans_kv_cache {
+  void* buf;            /* dev, onetrans_kv_cache_bytes(cfg, n_users) bytes */
+  size_t bytes;
+  int32_t n_users;
+  int32_t n_appended;   /* events appended since the prefill (same for all users) */
+  int32_t prefilled;    /* 1 after onetrans_user_prefill */
+} onetrans_kv_cache;
+
+/* ---- sizing, packing, cache set-up (host calls) -------------------------- */
+
+/* Validates a config: ONETRANS_OK or the reason it is not supported. */
+int onetrans_check_config(const onetrans_config* cfg);
+
+/* Bytes of the packed weight buffer the compute calls read. 0 on a bad config. */
+size_t onetrans_packed_weight_bytes(const onetrans_config* cfg);
+
+/* Converts the caller's per-layer weights (layers[cfg->n_layers]) into the
+ * packed device buffer `packed` (bf16 weights become fp16, E4M3FN codes and
+ * fp32 gains/scales are copied). Asynchronous on `stream`. The packed buffer
+ * must stay alive and unchanged while compute calls use it. */
+int onetrans_pack_weights(const onetrans_config* cfg, const onetrans_layer_weights* layers,
+                          void* packed, size_t packed_bytes, hipStream_t stream);
+
+/* Bytes of a K/V cache for n_users users. 0 on a bad config or n_users < 1. */
+size_t onetrans_kv_cache_bytes(const onetrans_config* cfg, int32_t n_users);
+
+/* Fills *out for a cache of n_users users in `buf` (no device work). */
+int onetrans_kv_cache_init(const onetrans_config* cfg, int32_t n_users, void* buf, size_t bytes,
+                           onetrans_kv_cache* out);
+
+/* Workspace bytes that cover every compute call with at most max_users users,
+ * max_candidates candidates per call and max_append appended events per call. */
+size_t onetrans_workspace_bytes(const onetrans_config* cfg, int32_t max_users,
+                                int32_t max_candidates, int32_t max_append);
+
+/* ---- compute calls (asynchronous on stream) ------------------------------ */
+
+/* User prefill: runs the S side of B users through every layer, writes each
+ * layer's K/V (all n_l input rows) into `cache` and returns the last layer's
+ * S outputs.
+ *   s_tokens  dev bf16 [B][s_len][d]; user u's history is right-aligned: its
+ *             s_lens[u] events sit in slots [s_len - s_lens[u], s_len); the
+ *             padding slots' contents are ignored (treated as zero)
+ *   s_lens    dev int32 [B]; values are clamped to [0, s_len]
+ *   s_out     dev fp32 [B][q_sched[L-1]][d]; rows of padding slots are 0
+ * The cache must have been initialised for at least B users; it is reset
+ * (n_appended = 0, prefilled = 1). */
+int onetrans_user_prefill(const onetrans_config* cfg, const void* packed,
+                          const uint16_t* s_tokens, const int32_t* s_lens, int32_t B,
+                          onetrans_kv_cache* cache, float* s_out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* KV append: m newly arrived events per user (for all cache->n_users users)
+ * enter every layer as queries at the next global positions; each sees the
+ * user's valid cached rows and the new events up to itself. Their K/V rows are
+ * appended in place and cache->n_appended grows by m (host-side, at enqueue).
+ *   new_tokens dev bf16 [B][m][d], B = cache->n_users
+ *   new_out    dev fp32 [B][m][d]: the new events' outputs after the last layer
+ * Returns ONETRANS_ERR_CAPACITY if n_appended + m > cfg->append_cap. */
+int onetrans_kv_append(const onetrans_config* cfg, const void* packed,
+                       const uint16_t* new_tokens, int32_t m, onetrans_kv_cache* cache,
+                       float* new_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Candidate scoring: the NS side of C candidates of user `user` against that
+ * user's cached S-side K/V (cross-request KV sharing).
+ *   ns_tokens dev bf16 [C][n_ns][d]
+ *   ns_out    dev fp32 [C][n_ns][d]: NS rows after the last layer
+ * C may be 0 (no work). */
+int onetrans_score_candidates(const onetrans_config* cfg, const void* packed,
+                              const onetrans_kv_cache* cache, int32_t user,
+                              const uint16_t* ns_tokens, int32_t C, float* ns_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Full pass without a persistent cache: prefill of B users into a cache held
+ * in the workspace, then scoring of each user's C candidates.
+ *   s_tokens, s_lens, s_out as in onetrans_user_prefill
+ *   ns_tokens dev bf16 [B][C][n_ns][d], ns_out dev fp32 [B][C][n_ns][d]
+ * Size the workspace with onetrans_block_forward_workspace_bytes. */
+size_t onetrans_block_forward_workspace_bytes(const onetrans_config* cfg, int32_t B, int32_t C);
+int onetrans_block_forward(const onetrans_config* cfg, const void* packed,
+                           const uint16_t* s_tokens, const int32_t* s_lens, int32_t B,
+                           const uint16_t* ns_tokens, int32_t C, float* s_out, float* ns_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- diagnostics --------------------------------------------------------- */
+
+const char* onetrans_status_str(int status);
+const char* onetrans_last_error(void);
+
+/* Copies layer `layer`'s cached K and V rows [0, rows) of user `user` into
+ * k_out and v_out (dev bf16 [rows][d] each, heads concatenated along d), for
+ * inspection and tests. rows must not exceed the layer's filled length. */
+int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* cache, int32_t layer,
+                           int32_t user, int32_t rows, uint16_t* k_out, uint16_t* v_out,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ONETRANS_H */

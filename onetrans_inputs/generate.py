@@ -36,9 +36,10 @@ E4M3_MAX = 448.0
 def bf16_round(x) -> np.ndarray:
     """Round to the nearest bf16 value (ties to even); returned as float32."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(f.shape)
+    u = f.view(np.uint32)
+    # finite inputs only: the largest finite pattern plus the bias stays below 2^32
+    u = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).reshape(f.shape)
 
 
 def e4m3_quantize(w: np.ndarray):
@@ -62,27 +63,31 @@ def _streams(seed: int):
 
 def make_weights(wl: Workload, seed: int = 0, ns_private_gains: bool = False) -> List[Dict[str, np.ndarray]]:
     """Per-layer weight dicts (float32 arrays holding bf16 values, or uint8 E4M3 codes)."""
-    rng = _streams(seed)[0]
+    gen = _streams(seed)[0]
     d, F, P = wl.d_model, wl.ffn_hidden, wl.n_ns
-    sd = np.sqrt(1.0 / d)
-    gsd = np.sqrt(0.1)
+    sd = np.float32(np.sqrt(1.0 / d))
+    gsd = np.float32(np.sqrt(0.1))
+
+    def normal(shape):  # fp32 draws; weights are rounded to bf16 / E4M3 afterwards
+        return gen.standard_normal(shape, dtype=np.float32)
+
     layers = []
     for _ in range(wl.n_layers):
-        s_wq = rng.standard_normal((d, d)) * sd
-        s_wk = rng.standard_normal((d, d)) * sd
-        s_wv = rng.standard_normal((d, d)) * sd
-        s_w1 = rng.standard_normal((F, d)) * sd
-        s_w2 = rng.standard_normal((d, F)) * sd
-        g_a = (1.0 + rng.standard_normal(d) * gsd).astype(np.float32)
-        g_f = (1.0 + rng.standard_normal(d) * gsd).astype(np.float32)
-        ns_wq = rng.standard_normal((P, d, d)) * sd
-        ns_wk = rng.standard_normal((P, d, d)) * sd
-        ns_wv = rng.standard_normal((P, d, d)) * sd
-        ns_w1 = rng.standard_normal((P, F, d)) * sd
-        ns_w2 = rng.standard_normal((P, d, F)) * sd
+        s_wq = normal((d, d)) * sd
+        s_wk = normal((d, d)) * sd
+        s_wv = normal((d, d)) * sd
+        s_w1 = normal((F, d)) * sd
+        s_w2 = normal((d, F)) * sd
+        g_a = (1.0 + normal(d) * gsd).astype(np.float32)
+        g_f = (1.0 + normal(d) * gsd).astype(np.float32)
+        ns_wq = normal((P, d, d)) * sd
+        ns_wk = normal((P, d, d)) * sd
+        ns_wv = normal((P, d, d)) * sd
+        ns_w1 = normal((P, F, d)) * sd
+        ns_w2 = normal((P, d, F)) * sd
         if ns_private_gains:
-            ns_ga = (1.0 + rng.standard_normal((P, d)) * gsd).astype(np.float32)
-            ns_gf = (1.0 + rng.standard_normal((P, d)) * gsd).astype(np.float32)
+            ns_ga = (1.0 + normal((P, d)) * gsd).astype(np.float32)
+            ns_gf = (1.0 + normal((P, d)) * gsd).astype(np.float32)
         else:
             ns_ga = np.broadcast_to(g_a, (P, d)).copy()
             ns_gf = np.broadcast_to(g_f, (P, d)).copy()

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every output element; the full-size workloads run in the
+benchmark's launch configuration and compare sampled users / candidates that
+the oracle computes one by one. Bars: max-abs 3e-2 and relative L2 1e-2 on
+the fp32 outputs (5e-2 / 2e-2 with E4M3 NS weights).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from onetrans_inputs import (CANDIDATE_HEAVY_FP8, ONETRANS_L, ONETRANS_S, PREFILL_BATCH, TINY, Workload,
+                             make_append_tokens, make_ns_tokens, make_s_tokens)
+from helpers import EPS, assert_close, bf16_dev, model
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# small cases: ragged tiles, general NS counts, padding (including an empty
+# history), head_dim 32 and 64, pyramid drops to a single-digit tail
+SMALL = {
+    "a_dh32_P5": (Workload(name="a", n_layers=2, d_model=64, n_heads=2, ffn_hidden=128, s_len=300,
+                           q_sched=(250, 97), n_ns=5, n_users=3, n_candidates=7), [300, 41, 0]),
+    "b_dh64_P32": (Workload(name="b", n_layers=3, d_model=128, n_heads=2, ffn_hidden=256, s_len=200,
+                            q_sched=(200, 130, 3), n_ns=32, n_users=2, n_candidates=5), [200, 1]),
+    "c_fp8": (Workload(name="c", n_layers=3, d_model=128, n_heads=2, ffn_hidden=256, s_len=200,
+                       q_sched=(200, 130, 3), n_ns=32, n_users=2, n_candidates=5, ns_wdtype="e4m3"), [150, 200]),
+    "d_single": (Workload(name="d", n_layers=1, d_model=64, n_heads=1, ffn_hidden=64, s_len=1, q_sched=(1,),
+                          n_ns=1, n_users=1, n_candidates=1), [1]),
+    "e_P40": (Workload(name="e", n_layers=2, d_model=192, n_heads=3, ffn_hidden=192, s_len=70,
+                       q_sched=(64, 33), n_ns=40, n_users=1, n_candidates=3), [70]),
+    "tiny": (TINY, [64]),
+}
+
+
+def _inputs(wl, lens):
+    s, _ = make_s_tokens(wl)
+    lens = np.asarray(lens, np.int32)
+    for u in range(s.shape[0]):
+        s[u, : wl.s_len - lens[u]] = 0.0
+    return s, lens, make_ns_tokens(wl)
+
+
+def _dev(s, lens, ns):
+    return bf16_dev(s), torch.from_numpy(lens).cuda(), bf16_dev(ns)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_block_forward_matches_oracle(name):
+    wl, lens = SMALL[name]
+    print(f"case {name}", flush=True)
+    m, lay = model(wl, private_gains=(name == "c_fp8"))
+    s, lens, ns = _inputs(wl, lens)
+    s_out, ns_out = m.block_forward(*_dev(s, lens, ns))
+    torch.cuda.synchronize()
+    ref_t, ref_n = O.block_forward(lay, wl.q_sched, wl.n_heads, EPS, s, lens, ns)
+    assert_close(s_out.cpu().numpy(), ref_t, wl.ns_wdtype, "S tail")
+    assert_close(ns_out.cpu().numpy(), ref_n, wl.ns_wdtype, "NS out")
+    # padding rows of the S tail are exactly zero
+    qL = wl.q_sched[-1]
+    for u, ln in enumerate(lens):
+        npad = min(qL, max(0, qL - int(ln)))
+        assert np.all(s_out[u, :npad].cpu().numpy() == 0.0)
+
+
+@pytest.mark.parametrize("name", ["a_dh32_P5", "b_dh64_P32", "c_fp8", "tiny"])
+def test_prefill_append_score_match_oracle(name):
+    wl, lens = SMALL[name]
+    print(f"case {name}", flush=True)
+    m1, m2 = 13, 6
+    mdl, lay = model(wl, append_cap=m1 + m2 + 1, private_gains=(name == "c_fp8"))
+    s, lens, ns = _inputs(wl, lens)
+    sd, ld, nd = _dev(s, lens, ns)
+    B = s.shape[0]
+    cache = mdl.new_cache(B)
+    s_out = mdl.user_prefill(sd, ld, cache)
+    new1 = make_append_tokens(wl, m=m1)
+    new2 = make_append_tokens(wl, seed=1, m=m2)
+    out1 = mdl.kv_append(bf16_dev(new1), cache)
+    out2 = mdl.kv_append(bf16_dev(new2), cache)
+    assert cache.n_appended == m1 + m2
+    scores = [mdl.score_candidates(cache, u, nd[u]) for u in range(B)]
+    torch.cuda.synchronize()
+    for u in range(B):
+        oc, ot = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[u], int(lens[u]))
+        assert_close(s_out[u].cpu().numpy(), ot, wl.ns_wdtype, f"user {u} S tail")
+        oc, o1 = O.append(lay, wl.n_heads, EPS, oc, new1[u])
+        oc, o2 = O.append(lay, wl.n_heads, EPS, oc, new2[u])
+        assert_close(out1[u].cpu().numpy(), o1, wl.ns_wdtype, f"user {u} append 1")
+        assert_close(out2[u].cpu().numpy(), o2, wl.ns_wdtype, f"user {u} append 2")
+        assert_close(scores[u].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, ns[u]), wl.ns_wdtype,
+                     f"user {u} score after appends")
+        for l in (0, wl.n_layers - 1):
+            rows = oc.length(l)
+            k, v = cache.read_layer(l, u, rows)
+            ok = (oc.base[l] + np.arange(rows)) >= oc.valid_from
+            assert_close(k.float().cpu().numpy()[ok], oc.k[l][ok], "bf16", f"user {u} layer {l} cached K")
+            assert_close(v.float().cpu().numpy()[ok], oc.v[l][ok], "bf16", f"user {u} layer {l} cached V")
+
+
+def test_zero_candidates_and_capacity_errors():
+    from unified_transformer_recommender_onetrans_amd import OneTransError
+    wl, lens = SMALL["b_dh64_P32"]
+    mdl, _ = model(wl, append_cap=4)
+    s, lens, ns = _inputs(wl, lens)
+    sd, ld, nd = _dev(s, lens, ns)
+    cache = mdl.new_cache(2)
+    mdl.user_prefill(sd, ld, cache)
+    out = mdl.score_candidates(cache, 0, nd[0][:0])
+    assert out.shape == (0, wl.n_ns, wl.d_model)
+    with pytest.raises(OneTransError):
+        mdl.kv_append(bf16_dev(make_append_tokens(wl, n_users=2, m=5)), cache)
+    assert cache.n_appended == 0
+    with pytest.raises(OneTransError):
+        mdl.score_candidates(cache, 2, nd[0])
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+# ---------------------------------------------------------------------------
+
+def test_causality_bit_exact():
+    wl, lens = SMALL["b_dh64_P32"]
+    mdl, _ = model(wl)
+    s, lens, ns = _inputs(wl, [200, 200])
+    base_t, base_n = mdl.block_forward(*_dev(s, lens, ns))
+    j = wl.s_len - 2            # perturb the second-to-last event of user 0
+    s2 = s.copy()
+    s2[0, j] += 1.0
+    t2, n2 = mdl.block_forward(*_dev(s2, lens, ns))
+    torch.cuda.synchronize()
+    tail_pos = np.arange(wl.s_len - wl.q_sched[-1], wl.s_len)
+    before = tail_pos < j
+    assert torch.equal(t2[0][before], base_t[0][before])
+    assert (t2[0][~before] - base_t[0][~before]).abs().amax(dim=1).min() > 0
+    assert (n2[0] - base_n[0]).abs().amax(dim=-1).min() > 0
+    assert torch.equal(t2[1], base_t[1]) and torch.equal(n2[1], base_n[1])
+
+
+def test_score_equals_block_forward_and_subsets():
+    wl, lens = SMALL["b_dh64_P32"]
+    mdl, _ = model(wl)
+    s, lens, ns = _inputs(wl, lens)
+    sd, ld, nd = _dev(s, lens, ns)
+    _, ns_bf = mdl.block_forward(sd, ld, nd)
+    cache = mdl.new_cache(2)
+    mdl.user_prefill(sd, ld, cache)
+    for u in range(2):
+        full = mdl.score_candidates(cache, u, nd[u])
+        assert torch.equal(full, ns_bf[u])
+        sub = mdl.score_candidates(cache, u, nd[u][1:4].contiguous())
+        assert torch.equal(sub, full[1:4])
+        perm = torch.tensor([3, 0, 4, 1, 2], device="cuda")
+        assert torch.equal(mdl.score_candidates(cache, u, nd[u][perm].contiguous()), full[perm])
+
+
+def test_append_equals_reprefill_on_gpu():
+    wl, lens = SMALL["b_dh64_P32"]
+    m = 9
+    mdl, _ = model(wl, append_cap=m)
+    s, lens, ns = _inputs(wl, lens)
+    cache = mdl.new_cache(2)
+    mdl.user_prefill(bf16_dev(s), torch.from_numpy(lens).cuda(), cache)
+    new = make_append_tokens(wl, n_users=2, m=m)
+    got = mdl.kv_append(bf16_dev(new), cache)
+    wl2 = wl.with_(s_len=wl.s_len + m, q_sched=tuple(q + m for q in wl.q_sched))
+    mdl2, _ = model(wl2)
+    cache2 = mdl2.new_cache(2)
+    tail2 = mdl2.user_prefill(bf16_dev(np.concatenate([s, new], axis=1)), torch.from_numpy(lens + m).cuda(), cache2)
+    sc1 = mdl.score_candidates(cache, 1, bf16_dev(ns[1]))
+    sc2 = mdl2.score_candidates(cache2, 1, bf16_dev(ns[1]))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(got.cpu().numpy(), tail2[:, -m:].cpu().numpy(), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(sc1.cpu().numpy(), sc2.cpu().numpy(), rtol=0, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (benchmark launch configuration), sampled outputs
+# ---------------------------------------------------------------------------
+
+def _score_sampled(wl, sample):
+    print(f"workload {wl.name}: C={wl.n_candidates}", flush=True)
+    mdl, lay = model(wl)
+    s, lens = make_s_tokens(wl)
+    ns = make_ns_tokens(wl)
+    cache = mdl.new_cache(1)
+    tail = mdl.user_prefill(bf16_dev(s), torch.from_numpy(lens).cuda(), cache)
+    out = mdl.score_candidates(cache, 0, bf16_dev(ns[0]))
+    torch.cuda.synchronize()
+    oc, ot = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[0], int(lens[0]))
+    assert_close(tail[0].cpu().numpy(), ot, "bf16", "S tail")
+    ref = O.score(lay, wl.n_heads, EPS, oc, ns[0][sample])
+    assert_close(out[sample].cpu().numpy(), ref, wl.ns_wdtype, f"candidates {list(sample)}")
+    return out
+
+
+def test_onetrans_s_full_size_sampled():
+    _score_sampled(ONETRANS_S, np.array([0, 37, 90, 127]))
+
+
+def test_onetrans_l_full_size_sampled():
+    _score_sampled(ONETRANS_L, np.array([0, 1, 100, 201, 255]))
+
+
+def test_candidate_heavy_fp8_full_size_sampled():
+    _score_sampled(CANDIDATE_HEAVY_FP8, np.array([0, 511, 1024, 2047, 3000, 4095]))
+
+
+def test_prefill_batch_and_append_full_size_sampled():
+    wl = PREFILL_BATCH
+    print(f"workload {wl.name}: B={wl.n_users} m={wl.append_m}", flush=True)
+    mdl, lay = model(wl, append_cap=wl.append_m)
+    s, lens = make_s_tokens(wl)
+    new = make_append_tokens(wl)
+    cache = mdl.new_cache(wl.n_users)
+    tail = mdl.user_prefill(bf16_dev(s), torch.from_numpy(lens).cuda(), cache)
+    got = mdl.kv_append(bf16_dev(new), cache)
+    torch.cuda.synchronize()
+    for u in (0, int(np.argmin(lens)), 63):
+        oc, ot = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[u], int(lens[u]))
+        assert_close(tail[u].cpu().numpy(), ot, "bf16", f"user {u} (len {lens[u]}) S tail")
+        oc, on = O.append(lay, wl.n_heads, EPS, oc, new[u])
+        assert_close(got[u].cpu().numpy(), on, "bf16", f"user {u} appended rows")
+        l = wl.n_layers - 1
+        k, v = cache.read_layer(l, u, oc.length(l))
+        ok = (oc.base[l] + np.arange(oc.length(l))) >= oc.valid_from
+        assert_close(k.float().cpu().numpy()[ok], oc.k[l][ok], "bf16", f"user {u} last-layer cached K")
+        assert_close(v.float().cpu().numpy()[ok], oc.v[l][ok], "bf16", f"user {u} last-layer cached V")

@@ -1,0 +1,573 @@
+// C ABI of the OneTrans block forward: validation, memory layouts and the
+// per-layer launch sequence. Every step of the computation runs in the HIP
+// kernels of gemm.hip, attention.hip and elementwise.hip.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/onetrans.h"
+#include "internal.h"
+
+using namespace onetrans;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+struct Shape {
+  int L, d, H, dh, F, P, s_len, append_cap;
+  int q[ONETRANS_MAX_LAYERS], n[ONETRANS_MAX_LAYERS], cap[ONETRANS_MAX_LAYERS];
+  bool fp8;
+  float eps;
+};
+
+int make_shape(const onetrans_config* c, Shape& s) {
+  if (!c) return fail(ONETRANS_ERR_INVALID_ARG, "config is NULL");
+  if (c->n_layers < 1 || c->n_layers > ONETRANS_MAX_LAYERS)
+    return fail(ONETRANS_ERR_UNSUPPORTED, "n_layers must be in [1, 16]");
+  if (c->d_model < 64 || c->d_model > 1024 || c->d_model % 64)
+    return fail(ONETRANS_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in [64, 1024]");
+  if (c->n_heads < 1 || c->d_model % c->n_heads)
+    return fail(ONETRANS_ERR_UNSUPPORTED, "n_heads must divide d_model");
+  const int dh = c->d_model / c->n_heads;
+  if (dh != 32 && dh != 64) return fail(ONETRANS_ERR_UNSUPPORTED, "head_dim must be 32 or 64");
+  if (c->ffn_hidden < 64 || c->ffn_hidden % 64) return fail(ONETRANS_ERR_UNSUPPORTED, "ffn_hidden must be a positive multiple of 64");
+  if (c->n_ns < 1 || c->n_ns > 256) return fail(ONETRANS_ERR_UNSUPPORTED, "n_ns must be in [1, 256]");
+  if (c->s_len < 1 || c->s_len > (1 << 20)) return fail(ONETRANS_ERR_UNSUPPORTED, "s_len must be in [1, 2^20]");
+  if (c->append_cap < 0 || c->append_cap > (1 << 20)) return fail(ONETRANS_ERR_UNSUPPORTED, "append_cap must be in [0, 2^20]");
+  if (!(c->rms_eps > 0.f) || !isfinite(c->rms_eps)) return fail(ONETRANS_ERR_INVALID_ARG, "rms_eps must be positive and finite");
+  if (c->ns_wdtype != ONETRANS_W_BF16 && c->ns_wdtype != ONETRANS_W_FP8_E4M3)
+    return fail(ONETRANS_ERR_UNSUPPORTED, "ns_wdtype must be ONETRANS_W_BF16 or ONETRANS_W_FP8_E4M3");
+  s.L = c->n_layers; s.d = c->d_model; s.H = c->n_heads; s.dh = dh; s.F = c->ffn_hidden; s.P = c->n_ns;
+  s.s_len = c->s_len; s.append_cap = c->append_cap; s.fp8 = c->ns_wdtype == ONETRANS_W_FP8_E4M3; s.eps = c->rms_eps;
+  int prev = c->s_len;
+  for (int l = 0; l < s.L; ++l) {
+    const int q = c->q_sched[l];
+    if (q < 1 || q > prev)
+      return fail(ONETRANS_ERR_UNSUPPORTED, "q_sched must satisfy 1 <= q_sched[l] <= q_sched[l-1] (q_sched[0] <= s_len)");
+    s.n[l] = prev;
+    s.q[l] = q;
+    s.cap[l] = (prev + s.append_cap + 63) / 64 * 64;  // tiles of 64 keys never read past the layer's block
+    prev = q;
+  }
+  return ONETRANS_OK;
+}
+
+struct LayerOffsets {
+  size_t s_wqkv, s_w1, s_w2, s_ga, s_gf, ns_wqkv, ns_w1, ns_w2, ns_scale, ns_ga, ns_gf;
+};
+
+// Packed buffer: per layer, fp16 S weights, fp32 S gains, fp16 (or E4M3 codes) NS
+// weights, fp32 NS scales and gains; every array starts on a 256-byte boundary.
+size_t packed_layout(const Shape& s, LayerOffsets* lo) {
+  size_t off = 0;
+  const size_t d = s.d, F = s.F, P = s.P, nsb = s.fp8 ? 1 : 2;
+  for (int l = 0; l < s.L; ++l) {
+    LayerOffsets o;
+    o.s_wqkv = off; off = align_up(off + 3 * d * d * 2);
+    o.s_w1 = off; off = align_up(off + F * d * 2);
+    o.s_w2 = off; off = align_up(off + d * F * 2);
+    o.s_ga = off; off = align_up(off + d * 4);
+    o.s_gf = off; off = align_up(off + d * 4);
+    o.ns_wqkv = off; off = align_up(off + P * 3 * d * d * nsb);
+    o.ns_w1 = off; off = align_up(off + P * F * d * nsb);
+    o.ns_w2 = off; off = align_up(off + P * d * F * nsb);
+    o.ns_scale = off; off = align_up(off + P * 5 * 4);
+    o.ns_ga = off; off = align_up(off + P * d * 4);
+    o.ns_gf = off; off = align_up(off + P * d * 4);
+    if (lo) lo[l] = o;
+  }
+  return off;
+}
+
+// Cache buffer: valid_from int32 [B], then per layer K bf16 [B][H][cap_l][dh]
+// and V^T bf16 [B][H][dh][cap_l].
+size_t cache_layout(const Shape& s, int B, size_t* k_off, size_t* v_off) {
+  size_t off = align_up((size_t)B * 4);
+  for (int l = 0; l < s.L; ++l) {
+    const size_t blk = (size_t)B * s.H * s.cap[l] * s.dh * 2;
+    if (k_off) k_off[l] = off;
+    off = align_up(off + blk);
+    if (v_off) v_off[l] = off;
+    off = align_up(off + blk);
+  }
+  return off;
+}
+
+struct PrefillWs { size_t x, q, hid, total; };
+PrefillWs prefill_ws(const Shape& s, int B) {
+  PrefillWs w;
+  size_t off = 0;
+  w.x = off; off = align_up(off + (size_t)B * s.s_len * s.d * 4);
+  w.q = off; off = align_up(off + (size_t)B * s.H * s.q[0] * s.dh * 2);
+  w.hid = off; off = align_up(off + (size_t)B * s.q[0] * s.F * 2);
+  w.total = off;
+  return w;
+}
+
+struct AppendWs { size_t q, hid, total; };
+AppendWs append_ws(const Shape& s, int B, int m) {
+  AppendWs w;
+  size_t off = 0;
+  w.q = off; off = align_up(off + (size_t)B * s.H * m * s.dh * 2);
+  w.hid = off; off = align_up(off + (size_t)B * m * s.F * 2);
+  w.total = off;
+  return w;
+}
+
+struct ScoreWs { size_t qn, kn, vn, hid, total; };
+ScoreWs score_ws(const Shape& s, int C) {
+  ScoreWs w;
+  size_t off = 0;
+  const size_t rows = (size_t)C * s.P;
+  w.qn = off; off = align_up(off + rows * s.d * 2);
+  w.kn = off; off = align_up(off + rows * s.d * 2);
+  w.vn = off; off = align_up(off + rows * s.d * 2);
+  w.hid = off; off = align_up(off + rows * s.F * 2);
+  w.total = off;
+  return w;
+}
+
+GemmParams base_gemm(const Shape& s) {
+  GemmParams g;
+  memset(&g, 0, sizeof(g));
+  g.d = s.d;
+  g.dh = s.dh;
+  g.eps = s.eps;
+  g.scale_col_div = 1 << 30;
+  g.groups = 1;
+  return g;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ONETRANS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return ONETRANS_OK;
+}
+
+#define OT_HIP(call, what)                      \
+  do {                                          \
+    int rc_ = hip_check((call), (what));        \
+    if (rc_ != ONETRANS_OK) return rc_;         \
+  } while (0)
+
+float scale_log2(const Shape& s) { return (float)(1.4426950408889634 / sqrt((double)s.dh)); }
+
+// ---- one S-side layer over `rows` rows per user (prefill: the layer input;
+// append: the new events), queries are the last `q` of them ----
+struct SLayerArgs {
+  int B, rows, q;
+  float* x; long x_seg_stride, x_row_base;  // residual rows of user u: x + u*x_seg_stride + (x_row_base + t)*d
+  __bf16* k; __bf16* vt; int cap, slot_base, n_keys, key_pos0;
+  const int* valid_from;
+  __bf16* qbuf; _Float16* hid;
+};
+
+int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SLayerArgs& a, hipStream_t st) {
+  const long d = s.d;
+  RowMap all{a.rows, 1, a.x_seg_stride, a.x_row_base, d, 0};
+  RowMap tail{a.q, 1, a.x_seg_stride, a.x_row_base + (a.rows - a.q), d, 0};
+
+  GemmParams g = base_gemm(s);
+  g.M = a.B * a.rows; g.N = 3 * s.d; g.K = s.d;
+  g.rm = all;
+  g.res_in = a.x; g.gain = (const float*)(pk + lo.s_ga);
+  g.w = pk + lo.s_wqkv;
+  g.q = a.qbuf; g.q_seg_stride = (long)s.H * a.q * s.dh; g.q_head_stride = (long)a.q * s.dh; g.q_from = a.rows - a.q;
+  g.k = a.k; g.vt = a.vt; g.kv_seg_stride = (long)s.H * a.cap * s.dh; g.kv_head_stride = (long)a.cap * s.dh;
+  g.kv_cap = a.cap; g.kv_slot_base = a.slot_base;
+  OT_HIP(launch_gemm(GEMM_QKV, false, g, st), "S QKV GEMM launch");
+
+  AttnParams at;
+  memset(&at, 0, sizeof(at));
+  at.nq = a.q; at.H = s.H; at.d = s.d;
+  at.q = a.qbuf; at.q_seg_stride = g.q_seg_stride; at.q_head_stride = g.q_head_stride;
+  at.res = a.x; at.res_seg_stride = a.x_seg_stride; at.res_row_base = tail.res_row_base; at.res_row_stride = d;
+  at.k = a.k; at.vt = a.vt; at.kv_seg_stride = g.kv_seg_stride; at.kv_head_stride = g.kv_head_stride; at.kv_cap = a.cap;
+  at.n_keys = a.n_keys; at.key_pos0 = a.key_pos0;
+  at.q_pos0 = a.key_pos0 + a.slot_base + (a.rows - a.q);
+  at.valid_from = a.valid_from;
+  at.P = 1;
+  at.scale_log2 = scale_log2(s);
+  OT_HIP(launch_attention(false, s.dh, at, a.B, st), "S attention launch");
+
+  GemmParams u = base_gemm(s);
+  u.M = a.B * a.q; u.N = s.F; u.K = s.d;
+  u.rm = tail;
+  u.res_in = a.x; u.gain = (const float*)(pk + lo.s_gf);
+  u.w = pk + lo.s_w1;
+  u.hid_out = a.hid;
+  OT_HIP(launch_gemm(GEMM_FFN_UP, false, u, st), "S FFN up launch");
+
+  GemmParams dn = base_gemm(s);
+  dn.M = a.B * a.q; dn.N = s.d; dn.K = s.F;
+  dn.rm = tail;
+  dn.hid_in = a.hid;
+  dn.w = pk + lo.s_w2;
+  dn.res_out = a.x;
+  OT_HIP(launch_gemm(GEMM_FFN_DOWN, false, dn, st), "S FFN down launch");
+  return ONETRANS_OK;
+}
+
+int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const char* cache_buf, const size_t* k_off,
+               const size_t* v_off, int n_users, int n_appended, int user, const uint16_t* ns_tokens, int C,
+               float* ns_out, char* ws, hipStream_t st) {
+  if (C == 0) return ONETRANS_OK;
+  const ScoreWs w = score_ws(s, C);
+  __bf16* qn = (__bf16*)(ws + w.qn);
+  __bf16* kn = (__bf16*)(ws + w.kn);
+  __bf16* vn = (__bf16*)(ws + w.vn);
+  _Float16* hid = (_Float16*)(ws + w.hid);
+  const long d = s.d, P = s.P, rows = (long)C * P;
+  const int* vf = (const int*)cache_buf;
+  OT_HIP(launch_bf16_to_f32(ns_tokens, ns_out, rows * d, st), "NS input conversion launch");
+  const RowMap rm{C, s.P, 0, 0, P * d, d};
+  for (int l = 0; l < s.L; ++l) {
+    const long cap = s.cap[l];
+    const int len = s.n[l] + n_appended;
+    GemmParams g = base_gemm(s);
+    g.M = C; g.N = 3 * s.d; g.K = s.d; g.groups = s.P;
+    g.rm = rm;
+    g.res_in = ns_out; g.gain = (const float*)(pk + lo[l].ns_ga); g.gain_group_stride = d;
+    g.w = pk + lo[l].ns_wqkv; g.w_group_stride = 3 * d * d;
+    g.wscale = (const float*)(pk + lo[l].ns_scale); g.scale_idx0 = 0; g.scale_col_div = s.d;
+    g.q = qn; g.q_seg_stride = 0; g.q_head_stride = rows * s.dh; g.q_from = 0;
+    g.k = kn; g.vt = vn; g.kv_seg_stride = 0; g.kv_head_stride = rows * s.dh; g.kv_cap = (int)rows; g.kv_slot_base = 0;
+    OT_HIP(launch_gemm(GEMM_QKV, s.fp8, g, st), "NS QKV GEMM launch");
+
+    AttnParams at;
+    memset(&at, 0, sizeof(at));
+    at.nq = (int)rows; at.H = s.H; at.d = s.d;
+    at.q = qn; at.q_seg_stride = 0; at.q_head_stride = rows * s.dh;
+    at.res = ns_out; at.res_seg_stride = 0; at.res_row_base = 0; at.res_row_stride = d;
+    const long user_off = (long)user * s.H * cap * s.dh;
+    at.k = (const __bf16*)(cache_buf + k_off[l]) + user_off;
+    at.vt = (const __bf16*)(cache_buf + v_off[l]) + user_off;
+    at.kv_seg_stride = 0; at.kv_head_stride = cap * s.dh; at.kv_cap = (int)cap;
+    at.n_keys = len; at.key_pos0 = s.s_len - s.n[l]; at.q_pos0 = 0;
+    at.valid_from = vf + user;
+    at.kn = kn; at.vtn = vn; at.kn_head_stride = rows * s.dh; at.P = s.P;
+    at.scale_log2 = scale_log2(s);
+    OT_HIP(launch_attention(true, s.dh, at, 1, st), "NS attention launch");
+
+    GemmParams u = base_gemm(s);
+    u.M = C; u.N = s.F; u.K = s.d; u.groups = s.P;
+    u.rm = rm;
+    u.res_in = ns_out; u.gain = (const float*)(pk + lo[l].ns_gf); u.gain_group_stride = d;
+    u.w = pk + lo[l].ns_w1; u.w_group_stride = (long)s.F * d;
+    u.wscale = (const float*)(pk + lo[l].ns_scale); u.scale_idx0 = 3;
+    u.hid_out = hid;
+    OT_HIP(launch_gemm(GEMM_FFN_UP, s.fp8, u, st), "NS FFN up launch");
+
+    GemmParams dn = base_gemm(s);
+    dn.M = C; dn.N = s.d; dn.K = s.F; dn.groups = s.P;
+    dn.rm = rm;
+    dn.hid_in = hid;
+    dn.w = pk + lo[l].ns_w2; dn.w_group_stride = d * s.F;
+    dn.wscale = (const float*)(pk + lo[l].ns_scale); dn.scale_idx0 = 4;
+    dn.res_out = ns_out;
+    OT_HIP(launch_gemm(GEMM_FFN_DOWN, s.fp8, dn, st), "NS FFN down launch");
+  }
+  (void)n_users;
+  return ONETRANS_OK;
+}
+
+int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const uint16_t* s_tokens,
+                 const int32_t* s_lens, int B, char* cache_buf, const size_t* k_off, const size_t* v_off,
+                 float* s_out, char* ws, hipStream_t st) {
+  const PrefillWs w = prefill_ws(s, B);
+  float* x = (float*)(ws + w.x);
+  int* vf = (int*)cache_buf;
+  OT_HIP(launch_s_input(s_tokens, s_lens, x, vf, B, s.s_len, s.d, st), "S input conversion launch");
+  for (int l = 0; l < s.L; ++l) {
+    SLayerArgs a;
+    a.B = B; a.rows = s.n[l]; a.q = s.q[l];
+    a.x = x; a.x_seg_stride = (long)s.s_len * s.d; a.x_row_base = s.s_len - s.n[l];
+    a.k = (__bf16*)(cache_buf + k_off[l]); a.vt = (__bf16*)(cache_buf + v_off[l]);
+    a.cap = s.cap[l]; a.slot_base = 0; a.n_keys = s.n[l]; a.key_pos0 = s.s_len - s.n[l];
+    a.valid_from = vf;
+    a.qbuf = (__bf16*)(ws + w.q); a.hid = (_Float16*)(ws + w.hid);
+    int rc = run_s_layer(s, pk, lo[l], a, st);
+    if (rc) return rc;
+  }
+  const int qL = s.q[s.L - 1];
+  OT_HIP(launch_copy_rows_f32(x + (long)(s.s_len - qL) * s.d, (long)s.s_len * s.d, s_out, (long)qL * s.d,
+                              (long)qL * s.d, B, st),
+         "S output copy launch");
+  return ONETRANS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* onetrans_status_str(int status) {
+  switch (status) {
+    case ONETRANS_OK: return "ok";
+    case ONETRANS_ERR_INVALID_ARG: return "invalid argument";
+    case ONETRANS_ERR_UNSUPPORTED: return "unsupported shape";
+    case ONETRANS_ERR_WORKSPACE: return "buffer too small";
+    case ONETRANS_ERR_CAPACITY: return "cache append capacity exceeded";
+    case ONETRANS_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* onetrans_last_error(void) { return g_last_error.c_str(); }
+
+int onetrans_check_config(const onetrans_config* cfg) {
+  Shape s;
+  return make_shape(cfg, s);
+}
+
+size_t onetrans_packed_weight_bytes(const onetrans_config* cfg) {
+  Shape s;
+  if (make_shape(cfg, s)) return 0;
+  return packed_layout(s, nullptr);
+}
+
+int onetrans_pack_weights(const onetrans_config* cfg, const onetrans_layer_weights* layers, void* packed,
+                          size_t packed_bytes, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, s);
+  if (rc) return rc;
+  if (!layers || !packed) return fail(ONETRANS_ERR_INVALID_ARG, "layers and packed must be non-NULL");
+  if (!aligned16(packed)) return fail(ONETRANS_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+  LayerOffsets lo[ONETRANS_MAX_LAYERS];
+  const size_t need = packed_layout(s, lo);
+  if (packed_bytes < need) return fail(ONETRANS_ERR_WORKSPACE, "packed buffer too small");
+  for (int l = 0; l < s.L; ++l) {
+    const onetrans_layer_weights& w = layers[l];
+    if (!w.s_wqkv || !w.s_w1 || !w.s_w2 || !w.s_g_attn || !w.s_g_ffn || !w.ns_wqkv || !w.ns_w1 || !w.ns_w2 ||
+        !w.ns_g_attn || !w.ns_g_ffn)
+      return fail(ONETRANS_ERR_INVALID_ARG, "layer " + std::to_string(l) + ": a weight pointer is NULL");
+    if (s.fp8 && !w.ns_scale) return fail(ONETRANS_ERR_INVALID_ARG, "E4M3 NS weights need ns_scale");
+    const void* ptrs[] = {w.s_wqkv, w.s_w1, w.s_w2, w.s_g_attn, w.s_g_ffn, w.ns_wqkv, w.ns_w1, w.ns_w2, w.ns_g_attn, w.ns_g_ffn};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return fail(ONETRANS_ERR_INVALID_ARG, "layer " + std::to_string(l) + ": weight pointers must be 16-byte aligned");
+  }
+  char* pk = (char*)packed;
+  const long d = s.d, F = s.F, P = s.P;
+  for (int l = 0; l < s.L; ++l) {
+    const onetrans_layer_weights& w = layers[l];
+    const LayerOffsets& o = lo[l];
+    OT_HIP(launch_bf16_to_f16((const uint16_t*)w.s_wqkv, (_Float16*)(pk + o.s_wqkv), 3 * d * d, stream), "pack");
+    OT_HIP(launch_bf16_to_f16((const uint16_t*)w.s_w1, (_Float16*)(pk + o.s_w1), F * d, stream), "pack");
+    OT_HIP(launch_bf16_to_f16((const uint16_t*)w.s_w2, (_Float16*)(pk + o.s_w2), d * F, stream), "pack");
+    OT_HIP(hipMemcpyAsync(pk + o.s_ga, w.s_g_attn, d * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
+    OT_HIP(hipMemcpyAsync(pk + o.s_gf, w.s_g_ffn, d * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
+    if (s.fp8) {
+      OT_HIP(hipMemcpyAsync(pk + o.ns_wqkv, w.ns_wqkv, P * 3 * d * d, hipMemcpyDeviceToDevice, stream), "pack copy");
+      OT_HIP(hipMemcpyAsync(pk + o.ns_w1, w.ns_w1, P * F * d, hipMemcpyDeviceToDevice, stream), "pack copy");
+      OT_HIP(hipMemcpyAsync(pk + o.ns_w2, w.ns_w2, P * d * F, hipMemcpyDeviceToDevice, stream), "pack copy");
+      OT_HIP(hipMemcpyAsync(pk + o.ns_scale, w.ns_scale, P * 5 * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
+    } else {
+      OT_HIP(launch_bf16_to_f16((const uint16_t*)w.ns_wqkv, (_Float16*)(pk + o.ns_wqkv), P * 3 * d * d, stream), "pack");
+      OT_HIP(launch_bf16_to_f16((const uint16_t*)w.ns_w1, (_Float16*)(pk + o.ns_w1), P * F * d, stream), "pack");
+      OT_HIP(launch_bf16_to_f16((const uint16_t*)w.ns_w2, (_Float16*)(pk + o.ns_w2), P * d * F, stream), "pack");
+    }
+    OT_HIP(hipMemcpyAsync(pk + o.ns_ga, w.ns_g_attn, P * d * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
+    OT_HIP(hipMemcpyAsync(pk + o.ns_gf, w.ns_g_ffn, P * d * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
+  }
+  return ONETRANS_OK;
+}
+
+size_t onetrans_kv_cache_bytes(const onetrans_config* cfg, int32_t n_users) {
+  Shape s;
+  if (make_shape(cfg, s) || n_users < 1) return 0;
+  return cache_layout(s, n_users, nullptr, nullptr);
+}
+
+int onetrans_kv_cache_init(const onetrans_config* cfg, int32_t n_users, void* buf, size_t bytes,
+                           onetrans_kv_cache* out) {
+  Shape s;
+  int rc = make_shape(cfg, s);
+  if (rc) return rc;
+  if (!buf || !out) return fail(ONETRANS_ERR_INVALID_ARG, "buf and out must be non-NULL");
+  if (!aligned16(buf)) return fail(ONETRANS_ERR_INVALID_ARG, "cache buffer must be 16-byte aligned");
+  if (n_users < 1) return fail(ONETRANS_ERR_INVALID_ARG, "n_users must be >= 1");
+  if (bytes < cache_layout(s, n_users, nullptr, nullptr)) return fail(ONETRANS_ERR_WORKSPACE, "cache buffer too small");
+  out->buf = buf;
+  out->bytes = bytes;
+  out->n_users = n_users;
+  out->n_appended = 0;
+  out->prefilled = 0;
+  return ONETRANS_OK;
+}
+
+size_t onetrans_workspace_bytes(const onetrans_config* cfg, int32_t max_users, int32_t max_candidates,
+                                int32_t max_append) {
+  Shape s;
+  if (make_shape(cfg, s) || max_users < 0 || max_candidates < 0 || max_append < 0) return 0;
+  size_t b = prefill_ws(s, max_users).total;
+  const size_t a = append_ws(s, max_users, max_append).total;
+  const size_t c = score_ws(s, max_candidates).total;
+  if (a > b) b = a;
+  if (c > b) b = c;
+  return b;
+}
+
+size_t onetrans_block_forward_workspace_bytes(const onetrans_config* cfg, int32_t B, int32_t C) {
+  Shape s;
+  if (make_shape(cfg, s) || B < 1 || C < 0) return 0;
+  size_t rest = prefill_ws(s, B).total;
+  const size_t c = score_ws(s, C).total;
+  if (c > rest) rest = c;
+  return cache_layout(s, B, nullptr, nullptr) + rest;
+}
+
+int onetrans_user_prefill(const onetrans_config* cfg, const void* packed, const uint16_t* s_tokens,
+                          const int32_t* s_lens, int32_t B, onetrans_kv_cache* cache, float* s_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, s);
+  if (rc) return rc;
+  if (!packed || !s_tokens || !s_lens || !cache || !cache->buf || !s_out || !workspace)
+    return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(packed) || !aligned16(s_tokens) || !aligned16(s_out) || !aligned16(workspace))
+    return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if (B < 1 || B > cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "B must be in [1, cache->n_users]");
+  if (cache->bytes < cache_layout(s, cache->n_users, nullptr, nullptr))
+    return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
+  if (workspace_bytes < prefill_ws(s, B).total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for prefill");
+  LayerOffsets lo[ONETRANS_MAX_LAYERS];
+  packed_layout(s, lo);
+  size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
+  cache_layout(s, cache->n_users, k_off, v_off);
+  rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, (char*)cache->buf, k_off, v_off, s_out,
+                    (char*)workspace, stream);
+  if (rc) return rc;
+  cache->n_appended = 0;
+  cache->prefilled = 1;
+  return ONETRANS_OK;
+}
+
+int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uint16_t* new_tokens, int32_t m,
+                       onetrans_kv_cache* cache, float* new_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, s);
+  if (rc) return rc;
+  if (!packed || !cache || !cache->buf) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!cache->prefilled) return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
+  if (m < 0) return fail(ONETRANS_ERR_INVALID_ARG, "m must be >= 0");
+  if (cache->n_appended + (long)m > s.append_cap) return fail(ONETRANS_ERR_CAPACITY, "append exceeds append_cap");
+  if (m == 0) return ONETRANS_OK;
+  if (!new_tokens || !new_out || !workspace) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(packed) || !aligned16(new_tokens) || !aligned16(new_out) || !aligned16(workspace))
+    return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  const int B = cache->n_users;
+  if (cache->bytes < cache_layout(s, B, nullptr, nullptr))
+    return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
+  const AppendWs w = append_ws(s, B, m);
+  if (workspace_bytes < w.total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for append");
+  LayerOffsets lo[ONETRANS_MAX_LAYERS];
+  packed_layout(s, lo);
+  size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
+  cache_layout(s, B, k_off, v_off);
+  char* cb = (char*)cache->buf;
+  char* ws = (char*)workspace;
+  OT_HIP(launch_bf16_to_f32(new_tokens, new_out, (long)B * m * s.d, stream), "append input conversion launch");
+  for (int l = 0; l < s.L; ++l) {
+    const int len = s.n[l] + cache->n_appended;
+    SLayerArgs a;
+    a.B = B; a.rows = m; a.q = m;
+    a.x = new_out; a.x_seg_stride = (long)m * s.d; a.x_row_base = 0;
+    a.k = (__bf16*)(cb + k_off[l]); a.vt = (__bf16*)(cb + v_off[l]);
+    a.cap = s.cap[l]; a.slot_base = len; a.n_keys = len + m; a.key_pos0 = s.s_len - s.n[l];
+    a.valid_from = (const int*)cb;
+    a.qbuf = (__bf16*)(ws + w.q); a.hid = (_Float16*)(ws + w.hid);
+    rc = run_s_layer(s, (const char*)packed, lo[l], a, stream);
+    if (rc) return rc;
+  }
+  cache->n_appended += m;
+  return ONETRANS_OK;
+}
+
+int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, const onetrans_kv_cache* cache,
+                              int32_t user, const uint16_t* ns_tokens, int32_t C, float* ns_out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, s);
+  if (rc) return rc;
+  if (!packed || !cache || !cache->buf) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!cache->prefilled) return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
+  if (user < 0 || user >= cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "user out of range");
+  if (C < 0) return fail(ONETRANS_ERR_INVALID_ARG, "C must be >= 0");
+  if (C == 0) return ONETRANS_OK;
+  if (!ns_tokens || !ns_out || !workspace) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(packed) || !aligned16(ns_tokens) || !aligned16(ns_out) || !aligned16(workspace))
+    return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if ((long)C * s.P > (1L << 26)) return fail(ONETRANS_ERR_UNSUPPORTED, "C * n_ns must be <= 2^26");
+  if (cache->bytes < cache_layout(s, cache->n_users, nullptr, nullptr))
+    return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
+  if (workspace_bytes < score_ws(s, C).total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for scoring");
+  LayerOffsets lo[ONETRANS_MAX_LAYERS];
+  packed_layout(s, lo);
+  size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
+  cache_layout(s, cache->n_users, k_off, v_off);
+  return score_impl(s, (const char*)packed, lo, (const char*)cache->buf, k_off, v_off, cache->n_users,
+                    cache->n_appended, user, ns_tokens, C, ns_out, (char*)workspace, stream);
+}
+
+int onetrans_block_forward(const onetrans_config* cfg, const void* packed, const uint16_t* s_tokens,
+                           const int32_t* s_lens, int32_t B, const uint16_t* ns_tokens, int32_t C, float* s_out,
+                           float* ns_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, s);
+  if (rc) return rc;
+  if (!packed || !s_tokens || !s_lens || !s_out || !workspace || (C > 0 && (!ns_tokens || !ns_out)))
+    return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(packed) || !aligned16(s_tokens) || !aligned16(s_out) || !aligned16(workspace) ||
+      (C > 0 && (!aligned16(ns_tokens) || !aligned16(ns_out))))
+    return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if (B < 1 || C < 0) return fail(ONETRANS_ERR_INVALID_ARG, "B must be >= 1 and C >= 0");
+  if ((long)C * s.P > (1L << 26)) return fail(ONETRANS_ERR_UNSUPPORTED, "C * n_ns must be <= 2^26");
+  if (workspace_bytes < onetrans_block_forward_workspace_bytes(cfg, B, C))
+    return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for block_forward");
+  LayerOffsets lo[ONETRANS_MAX_LAYERS];
+  packed_layout(s, lo);
+  size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
+  const size_t cache_bytes = cache_layout(s, B, k_off, v_off);
+  char* cb = (char*)workspace;
+  char* rest = cb + cache_bytes;
+  rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, cb, k_off, v_off, s_out, rest, stream);
+  if (rc) return rc;
+  const long per_user = (long)C * s.P * s.d;
+  for (int u = 0; u < B; ++u) {
+    rc = score_impl(s, (const char*)packed, lo, cb, k_off, v_off, B, 0, u, ns_tokens + u * per_user, C,
+                    ns_out + u * per_user, rest, stream);
+    if (rc) return rc;
+  }
+  return ONETRANS_OK;
+}
+
+int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* cache, int32_t layer, int32_t user,
+                           int32_t rows, uint16_t* k_out, uint16_t* v_out, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, s);
+  if (rc) return rc;
+  if (!cache || !cache->buf || !k_out || !v_out) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (layer < 0 || layer >= s.L) return fail(ONETRANS_ERR_INVALID_ARG, "layer out of range");
+  if (user < 0 || user >= cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "user out of range");
+  if (rows < 0 || rows > s.n[layer] + cache->n_appended) return fail(ONETRANS_ERR_INVALID_ARG, "rows beyond the filled length");
+  size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
+  cache_layout(s, cache->n_users, k_off, v_off);
+  const long uo = (long)user * s.H * s.cap[layer] * s.dh;
+  const char* cb = (const char*)cache->buf;
+  OT_HIP(launch_cache_read((const __bf16*)(cb + k_off[layer]) + uo, (const __bf16*)(cb + v_off[layer]) + uo, s.H, s.dh,
+                           s.cap[layer], rows, (__bf16*)k_out, (__bf16*)v_out, stream),
+         "cache read launch");
+  return ONETRANS_OK;
+}
+
+}  // extern "C"
