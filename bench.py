@@ -1,0 +1,361 @@
+"""Benchmark of the OneTrans block forward on one MI355X.
+
+One step = onetrans_block_forward on the OneTransL-shape workload: the S side of
+one user (1500 events, pyramid 1500 -> 16 over 8 layers) is prefilled into the
+K/V cache, then C = 256 candidates (32 NS tokens each) are scored against it.
+`value` is candidates scored per second over the timed steps; TFLOP/s counts
+the algorithmic work of the step (prefill + scoring). The same JSON line also
+carries:
+  roofline      the dominant kernel family, timed live with HIP events on the
+                library's stream during the timed steps, against MI355X peaks
+  scoring_only  candidate scoring against an already-filled cache (the serving
+                steady state the cross-request K/V sharing targets)
+  prefill_batch 64 users, lengths U{1000..1500}, prefill throughput
+  append        64 new events for each of those 64 users, appended to the cache
+  cpu_baseline  the fp64 oracle on the host cores on a bounded sample
+Inputs are seeded synthetic data with the workloads' shapes and distributions.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from onetrans_inputs import (CANDIDATE_HEAVY_FP8, ONETRANS_L, ONETRANS_S, PREFILL_BATCH,  # noqa: E402
+                             make_append_tokens, make_ns_tokens, make_s_tokens, make_weights)
+
+METRIC = "candidates scored/s + TFLOP/s (% bf16 MFMA peak), OneTransL-shape block fwd"
+PEAK_TFLOPS_16BIT = 2500.0     # MI355X dense fp16 / bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+RIDGE = PEAK_TFLOPS_16BIT * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work model: 2 flops per MAC of the projections / FFN over the rows
+# actually needed (valid events; queries only for Q and the FFN), 4*d flops per
+# visible (query, key) pair; padding, masked and pruned work excluded. Bytes:
+# each operand a kernel must read or write, once.
+# ---------------------------------------------------------------------------
+
+def layer_rows(wl):
+    n, prev = [], wl.s_len
+    for q in wl.q_sched:
+        n.append(prev)
+        prev = q
+    return n, list(wl.q_sched)
+
+
+def _valid(lo: int, hi: int, vf: int) -> int:
+    return max(0, hi - max(lo, vf))
+
+
+def prefill_flops(wl, lens) -> float:
+    d, F = wl.d_model, wl.ffn_hidden
+    n, q = layer_rows(wl)
+    tot = 0.0
+    for ln in lens:
+        vf = wl.s_len - int(ln)
+        for l in range(wl.n_layers):
+            base, qbase = wl.s_len - n[l], wl.s_len - q[l]
+            nv, qv = _valid(base, wl.s_len, vf), _valid(qbase, wl.s_len, vf)
+            kstart = max(base, vf)
+            first_q = wl.s_len - qv
+            lead = first_q - kstart          # keys before the first valid query
+            pairs = qv * (lead + 1) + qv * (qv - 1) / 2
+            tot += 2 * d * d * (2 * nv + qv) + 4 * d * pairs + 4 * d * F * qv
+    return tot
+
+
+def cache_valid_rows(wl, ln: int, n_appended: int = 0):
+    n, _ = layer_rows(wl)
+    vf = wl.s_len - int(ln)
+    return [_valid(wl.s_len - n[l], wl.s_len, vf) + n_appended for l in range(wl.n_layers)]
+
+
+def append_flops(wl, lens, m: int) -> float:
+    d, F = wl.d_model, wl.ffn_hidden
+    tot = 0.0
+    for ln in lens:
+        for nk in cache_valid_rows(wl, ln):
+            tot += 2 * d * 3 * d * m + 4 * d * (m * nk + m * (m + 1) / 2) + 4 * d * F * m
+    return tot
+
+
+def score_flops_per_candidate(wl, nk) -> float:
+    d, F, P = wl.d_model, wl.ffn_hidden, wl.n_ns
+    return sum(2 * d * 3 * d * P + 4 * d * (P * k + P * (P + 1) / 2) + 4 * d * F * P for k in nk)
+
+
+def kernel_work(wl, C: int, nk, lens=None, m: int = 0):
+    """Per-family algorithmic (flops, bytes) summed over one call's launches.
+
+    NS families: one scoring call of C candidates with valid cached rows nk[l].
+    S families: one prefill (lens given, m = 0) or one append of m events.
+    """
+    d, F, P, L = wl.d_model, wl.ffn_hidden, wl.n_ns, wl.n_layers
+    wb = 1 if wl.ns_wdtype == "e4m3" else 2
+    R = C * P
+    w = {}
+    if C:
+        w["ns_qkv"] = (L * 2 * R * d * 3 * d, L * (P * 3 * d * d * wb + R * d * 4 + R * 3 * d * 2 + P * d * 4))
+        w["ns_attn"] = (sum(4 * d * C * (P * k + P * (P + 1) / 2) for k in nk),
+                        sum(2 * k * d * 2 + R * 3 * d * 2 + R * d * 8 for k in nk))
+        w["ns_ffn_up"] = (L * 2 * R * d * F, L * (P * F * d * wb + R * d * 4 + R * F * 2 + P * d * 4))
+        w["ns_ffn_down"] = (L * 2 * R * F * d, L * (P * d * F * wb + R * F * 2 + R * d * 8))
+    if lens is not None:
+        n, q = layer_rows(wl)
+        fl = {"s_qkv": 0.0, "s_attn": 0.0, "s_ffn_up": 0.0, "s_ffn_down": 0.0}
+        by = dict(fl)
+        for ln in lens:
+            vf = wl.s_len - int(ln)
+            for l in range(L):
+                if m == 0:
+                    base, qbase = wl.s_len - n[l], wl.s_len - q[l]
+                    nv, qv = _valid(base, wl.s_len, vf), _valid(qbase, wl.s_len, vf)
+                    lead = (wl.s_len - qv) - max(base, vf)
+                    pairs = qv * (lead + 1) + qv * (qv - 1) / 2
+                    kv_read = nv
+                else:
+                    nv = qv = m
+                    nk_l = cache_valid_rows(wl, ln)[l]
+                    pairs = m * nk_l + m * (m + 1) / 2
+                    kv_read = nk_l + m
+                fl["s_qkv"] += 2 * d * d * (2 * nv + qv)
+                by["s_qkv"] += nv * d * 4 + (2 * nv + qv) * d * 2
+                fl["s_attn"] += 4 * d * pairs
+                by["s_attn"] += kv_read * d * 2 * 2 + qv * d * 2 + qv * d * 8
+                fl["s_ffn_up"] += 2 * d * F * qv
+                by["s_ffn_up"] += qv * d * 4 + qv * F * 2
+                fl["s_ffn_down"] += 2 * d * F * qv
+                by["s_ffn_down"] += qv * F * 2 + qv * d * 8
+        for l in range(L):  # shared S weights, once per launch
+            by["s_qkv"] += 3 * d * d * 2
+            by["s_ffn_up"] += F * d * 2
+            by["s_ffn_down"] += d * F * 2
+        for k in fl:
+            w[k] = (fl[k], by[k])
+    return w
+
+
+# ---------------------------------------------------------------------------
+
+def device_weights(raw, dev):
+    import torch
+    out = []
+    for lw in raw:
+        dd = {}
+        for k, v in lw.items():
+            if v is None:
+                dd[k] = None
+            elif v.dtype == np.uint8 or k.startswith(("s_g", "ns_g", "ns_scale")):
+                dd[k] = torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+            else:
+                dd[k] = torch.from_numpy(np.ascontiguousarray(v)).to(dev).to(torch.bfloat16)
+        out.append(dd)
+    return out
+
+
+def bf16(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+
+
+def timed(fn, steps, warmup, sync):
+    for _ in range(warmup):
+        fn()
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    sync()
+    return time.perf_counter() - t0
+
+
+def roofline_entry(family, flops, nbytes, ms, launches):
+    sec = ms / 1e3
+    intensity = flops / nbytes if nbytes else float("inf")
+    if intensity >= RIDGE:
+        ach = flops / sec / 1e12
+        return {"kernel": family, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_TFLOPS_16BIT,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS_16BIT, 4), "traffic": None,
+                "launches": launches, "avg_launch_us": round(ms / launches * 1e3, 2),
+                "algorithmic_flops_per_launch": flops / launches, "algorithmic_bytes_per_launch": nbytes / launches}
+    ach = nbytes / sec / 1e9
+    return {"kernel": family, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "launches": launches,
+            "avg_launch_us": round(ms / launches * 1e3, 2),
+            "algorithmic_flops_per_launch": flops / launches, "algorithmic_bytes_per_launch": nbytes / launches}
+
+
+def cpu_baseline(wl, raw, s, lens, ns, sample_c: int):
+    """The fp64 oracle (as it stands) on the host: prefill + scoring of a candidate sample."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    lay = O.layers_from_arrays(raw)
+    t0 = time.perf_counter()
+    cache, _ = O.prefill(lay, wl.q_sched, wl.n_heads, wl.rms_eps, s[0], int(lens[0]))
+    t1 = time.perf_counter()
+    O.score(lay, wl.n_heads, wl.rms_eps, cache, ns[0][:sample_c])
+    t2 = time.perf_counter()
+    C = ns.shape[1]
+    step = (t1 - t0) + (t2 - t1) * C / sample_c
+    return {"value": round(C / step, 2), "unit": "candidates/s", "cores": threads, "kind": "oracle",
+            "sample": f"one user's prefill + {sample_c} of {C} candidates scored; step time = prefill + "
+                      f"scoring time scaled linearly to C={C}",
+            "seconds": round(t2 - t0, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true", help="skip the prefill-batch / append / scoring-only parts")
+    ap.add_argument("--cpu-sample", type=int, default=96)
+    ap.add_argument("--workload", default="onetrans_l", choices=["onetrans_l", "onetrans_s", "candidate_heavy_fp8"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the multi-GPU design is "
+                                   "documented, not built)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import __graft_entry__
+    from unified_transformer_recommender_onetrans_amd import LIB_PATH, OneTrans, make_config
+    from unified_transformer_recommender_onetrans_amd._capi import (KERNEL_FAMILIES, kernel_timing_enable,
+                                                                     kernel_timing_read)
+    if not os.path.exists(LIB_PATH):
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    sync = lambda: torch.cuda.synchronize(dev)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    wl = {"onetrans_l": ONETRANS_L, "onetrans_s": ONETRANS_S, "candidate_heavy_fp8": CANDIDATE_HEAVY_FP8}[
+        args.workload]
+    C = wl.n_candidates
+    log(f"[bench] generating {wl.name} inputs")
+    raw = make_weights(wl)
+    s, lens = make_s_tokens(wl)
+    ns = make_ns_tokens(wl)
+    cfg = make_config(wl.n_layers, wl.d_model, wl.n_heads, wl.ffn_hidden, wl.n_ns, wl.s_len, wl.q_sched,
+                      rms_eps=wl.rms_eps, ns_wdtype=wl.ns_wdtype)
+    model = OneTrans(cfg, device_weights(raw, dev), device=dev)
+    s_d, l_d, ns_d = bf16(s, dev), torch.from_numpy(lens).to(dev), bf16(ns, dev)
+    step = lambda: model.block_forward(s_d, l_d, ns_d)
+
+    nk = cache_valid_rows(wl, int(lens[0]))
+    step_flops = prefill_flops(wl, lens) + C * score_flops_per_candidate(wl, nk)
+    work = kernel_work(wl, C, nk, lens=lens)
+
+    # warmup with every family timed: find the dominant kernel family
+    log("[bench] warmup")
+    kernel_timing_enable(KERNEL_FAMILIES)
+    for _ in range(max(1, args.warmup)):
+        step()
+    sync()
+    per_family = {f: kernel_timing_read(f) for f in KERNEL_FAMILIES}
+    nw = max(1, args.warmup)
+    breakdown = {f: round(ms / nw * 1e3, 1) for f, (ms, n) in per_family.items() if n}
+    dominant = max((f for f in per_family if f in work), key=lambda f: per_family[f][0])
+
+    # timed steps; the dominant family stays event-timed on the library's stream
+    log(f"[bench] timing {args.steps} steps (dominant kernel family: {dominant})")
+    kernel_timing_enable([dominant])
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    sync()
+    el = time.perf_counter() - t0
+    ms_dom, n_dom = kernel_timing_read(dominant)
+    kernel_timing_enable([])
+    fl, by = work[dominant]
+    roof = roofline_entry(dominant, fl * args.steps, by * args.steps, ms_dom, n_dom)
+
+    ms_step = el / args.steps * 1e3
+    tflops = step_flops / (el / args.steps) / 1e12
+    out = {
+        "metric": METRIC, "value": round(C * args.steps / el, 1), "unit": "candidates/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16/bf16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": f"{wl.name} block_forward: 1 user x {wl.s_len} S events (pyramid "
+                               f"{wl.q_sched[0]}->{wl.q_sched[-1]}, {wl.n_layers} layers, d={wl.d_model}, "
+                               f"{wl.n_heads} heads), C={C} candidates x {wl.n_ns} NS tokens"
+                               + (", E4M3 NS weights" if wl.ns_wdtype == "e4m3" else ""),
+                   "global_batch": C, "seq_len": wl.s_len + wl.n_ns},
+        "tflops": round(tflops, 2), "pct_bf16_mfma_peak": round(100 * tflops / PEAK_TFLOPS_16BIT, 2),
+        "step_gflop": round(step_flops / 1e9, 2),
+        "roofline": roof,
+        "kernel_us_per_step": breakdown,
+    }
+
+    if not args.no_sub:
+        # scoring only, cache filled once (untimed)
+        cache = model.new_cache(1)
+        model.user_prefill(s_d, l_d, cache)
+        sc_out = torch.empty(C, wl.n_ns, wl.d_model, dtype=torch.float32, device=dev)
+        sc = lambda: model.score_candidates(cache, 0, ns_d[0], out=sc_out)
+        el_s = timed(sc, args.steps, args.warmup, sync)
+        sflops = C * score_flops_per_candidate(wl, nk)
+        out["scoring_only"] = {"candidates_per_s": round(C * args.steps / el_s, 1),
+                               "ms_per_call": round(el_s / args.steps * 1e3, 4),
+                               "tflops": round(sflops / (el_s / args.steps) / 1e12, 2),
+                               "pct_bf16_mfma_peak": round(100 * sflops / (el_s / args.steps) / 1e12 /
+                                                           PEAK_TFLOPS_16BIT, 2)}
+        del cache
+        # prefill batch and append (64 users, lengths U{1000..1500}, then 64 new events each)
+        pw = PREFILL_BATCH
+        log("[bench] prefill batch / append")
+        ps, plens = make_s_tokens(pw)
+        pnew = make_append_tokens(pw)
+        cfg2 = make_config(pw.n_layers, pw.d_model, pw.n_heads, pw.ffn_hidden, pw.n_ns, pw.s_len, pw.q_sched,
+                           append_cap=pw.append_m, rms_eps=pw.rms_eps)
+        m2 = OneTrans(cfg2, device_weights(raw, dev), device=dev)
+        ps_d, pl_d, pn_d = bf16(ps, dev), torch.from_numpy(plens).to(dev), bf16(pnew, dev)
+        pcache = m2.new_cache(pw.n_users)
+        psteps = max(3, args.steps // 4)
+        el_p = timed(lambda: m2.user_prefill(ps_d, pl_d, pcache), psteps, 1, sync)
+        pfl = prefill_flops(pw, plens)
+        pt = pfl / (el_p / psteps) / 1e12
+
+        def app():
+            pcache.c.n_appended = 0  # rewrite the same rows each time: identical work per call
+            m2.kv_append(pn_d, pcache)
+        el_a = timed(app, psteps, 1, sync)
+        afl = append_flops(pw, plens, pw.append_m)
+        aw = kernel_work(pw, 0, None, lens=plens, m=pw.append_m)
+        abytes = sum(b for _, b in aw.values())
+        t_a = el_a / psteps
+        out["prefill_batch"] = {"users": pw.n_users, "prefills_per_s": round(pw.n_users / (el_p / psteps), 1),
+                                "ms_per_call": round(el_p / psteps * 1e3, 3), "tflops": round(pt, 2),
+                                "pct_bf16_mfma_peak": round(100 * pt / PEAK_TFLOPS_16BIT, 2)}
+        out["append"] = {"users": pw.n_users, "events_per_user": pw.append_m,
+                         "events_per_s": round(pw.n_users * pw.append_m / t_a, 1),
+                         "ms_per_call": round(t_a * 1e3, 4), "tflops": round(afl / t_a / 1e12, 2),
+                         "algorithmic_gbs": round(abytes / t_a / 1e9, 1),
+                         "pct_hbm_peak": round(100 * abytes / t_a / 1e9 / PEAK_HBM_GBS, 2)}
+        del m2, pcache
+
+    if not args.no_cpu_baseline:
+        log("[bench] oracle CPU baseline")
+        out["cpu_baseline"] = cpu_baseline(wl, raw, s, lens, ns, min(args.cpu_sample, C))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

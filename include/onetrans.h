@@ -197,6 +197,21 @@ int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* 
                            int32_t user, int32_t rows, uint16_t* k_out, uint16_t* v_out,
                            hipStream_t stream);
 
+/* Kernel timing (diagnostics). While a family's bit is set in `mask`
+ * (bit k = 1 << onetrans_kernel_family k), each launch of that family is
+ * bracketed by two HIP events recorded on the launch's stream. Enabling resets
+ * all totals; onetrans_kernel_timing_read waits for the recorded events of one
+ * family and returns the summed device milliseconds and the launch count since
+ * the reset. mask = 0 turns timing off. Process-wide, not thread-safe. */
+typedef enum {
+  ONETRANS_K_S_QKV = 0, ONETRANS_K_S_ATTN = 1, ONETRANS_K_S_FFN_UP = 2, ONETRANS_K_S_FFN_DOWN = 3,
+  ONETRANS_K_NS_QKV = 4, ONETRANS_K_NS_ATTN = 5, ONETRANS_K_NS_FFN_UP = 6, ONETRANS_K_NS_FFN_DOWN = 7,
+  ONETRANS_K_ELEMENTWISE = 8, ONETRANS_K_S_NORM = 9, ONETRANS_K_NS_NORM = 10, ONETRANS_K_NS_FFN = 11,
+  ONETRANS_K_COUNT = 12
+} onetrans_kernel_family;
+int onetrans_kernel_timing_enable(uint32_t mask);
+int onetrans_kernel_timing_read(int family, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

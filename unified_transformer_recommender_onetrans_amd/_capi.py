@@ -63,7 +63,29 @@ EXPORTS = {
     "onetrans_kv_cache_read": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(KVCache), ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p]),
+    "onetrans_kernel_timing_enable": (ctypes.c_int, [ctypes.c_uint32]),
+    "onetrans_kernel_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                                   ctypes.POINTER(ctypes.c_int64)]),
 }
+
+KERNEL_FAMILIES = ["s_qkv", "s_attn", "s_ffn_up", "s_ffn_down", "ns_qkv", "ns_attn", "ns_ffn_up", "ns_ffn_down",
+                   "elementwise", "s_norm", "ns_norm", "ns_ffn"]
+
+
+def kernel_timing_enable(families) -> None:
+    """Start per-launch event timing of the named kernel families (empty = off)."""
+    mask = 0
+    for f in families:
+        mask |= 1 << KERNEL_FAMILIES.index(f)
+    check(lib().onetrans_kernel_timing_enable(mask), "kernel_timing_enable")
+
+
+def kernel_timing_read(family: str):
+    """(total device milliseconds, launches) of one family since timing was enabled."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    check(lib().onetrans_kernel_timing_read(KERNEL_FAMILIES.index(family), ctypes.byref(ms), ctypes.byref(n)),
+          "kernel_timing_read")
+    return ms.value, n.value
 
 _lib = None
 

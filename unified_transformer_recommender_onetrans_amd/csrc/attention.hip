@@ -9,10 +9,14 @@
 // Layout trick: the kernel computes S^T = K Q^T and O^T = V^T P^T with
 // v_mfma_f32_32x32x16_bf16, so every lane owns one query (lane & 31) in all
 // three of S^T, P^T and O^T. The online-softmax max and sum stay inside a lane
-// pair (lane, lane ^ 32) and need one cross-lane exchange per key tile; P never
-// leaves registers. V is stored transposed ([dh][key]) so the V^T operand is a
-// plain row read. Each wave owns 32 queries; a workgroup of 4 waves shares the
-// K / V^T tiles (64 keys) staged through LDS. The result is added to the fp32
+// pair (lane, lane ^ 32) and need one cross-lane exchange per key block; P never
+// leaves registers. The cached V is stored transposed ([dh][key]) so the V^T
+// operand is a plain row read.
+//
+// Data movement: each wave owns 32 queries; a workgroup of 4 waves shares K and
+// V^T tiles of 64 keys that travel global -> LDS with global_load_lds_dwordx4,
+// three tiles in flight. Tile rows are XOR-swizzled in 16-byte chunks so the
+// fragment reads are bank-conflict free. The result is added to the fp32
 // residual rows (z = x + o) without rounding.
 #include <math.h>
 #include "internal.h"
@@ -24,7 +28,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int KT = 64;  // keys per LDS tile
+constexpr int KT = 64;      // keys per tile
+constexpr int STAGES = 3;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// barrier without the release fence of __syncthreads (see gemm.hip)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int DH>
 struct Softmax {
@@ -32,9 +50,9 @@ struct Softmax {
   f32x16 o[DH / 32];
 };
 
-// Online-softmax update with one 32-key block of scores already masked and
-// scaled into log2 units; returns the bf16 probabilities packed as the two
-// B operands (keys 0-15 and 16-31 of the block in the lane's slot order).
+// Online-softmax update with NB 32-key blocks of scores already masked and
+// scaled into log2 units; returns the bf16 probabilities packed as the B
+// operands (keys 0-15 and 16-31 of each block in the lane's slot order).
 template <int DH, int NB>
 __device__ __forceinline__ void softmax_update(Softmax<DH>& st, f32x16 (&sc)[NB], bf16x8 (&pb)[NB][2]) {
   float mt = -INFINITY;
@@ -68,10 +86,16 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, f32x16 (&sc)[NB]
 
 template <int DH, bool NS>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
-  constexpr int KLD = DH + 8;  // K tile row stride (bf16)
-  constexpr int VLD = KT + 8;  // V^T tile row stride (bf16)
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[KT * KLD];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[DH * VLD];
+  constexpr int KROW = DH * 2;                // bytes per K row (64 or 128)
+  constexpr int K_BYTES = KT * KROW;
+  constexpr int V_BYTES = DH * KT * 2;        // DH rows of 64 keys (128 B)
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int K_INSTR = K_BYTES / 1024 / 4;
+  constexpr int V_INSTR = V_BYTES / 1024 / 4;
+  constexpr int PER_TILE = K_INSTR + V_INSTR;
+  constexpr int KCH = KROW / 16;              // 16-byte chunks per K row
+  constexpr int KRPI = 64 / KCH;              // K rows per wave instruction
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -116,44 +140,58 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) st.o[db][j] = 0.f;
 
-  const __bf16* kbase = p.k + seg * p.kv_seg_stride + h * p.kv_head_stride;
-  const __bf16* vbase = p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride;
+  // ---- per-lane sources of the tile DMA (slots beyond the filled length hold zeros) ----
+  const char* kbase = (const char*)(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride);
+  const char* vbase = (const char*)(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride);
+  long k_off[K_INSTR], v_off[V_INSTR];
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) {
+    const int r = (wave * K_INSTR + i) * KRPI + lane / KCH;
+    const int c = lane % KCH;
+    const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+    k_off[i] = (long)r * KROW + cs * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < V_INSTR; ++i) {
+    const int r = (wave * V_INSTR + i) * 8 + (lane >> 3);   // dh row
+    v_off[i] = (long)r * p.kv_cap * 2 + ((((lane & 7) ^ ((r >> 1) & 7))) << 4);
+  }
+  auto issue = [&](int t0, int stage) {
+    char* sb = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < K_INSTR; ++i)
+      dma16(kbase + (long)t0 * KROW + k_off[i], (lds_void*)(sb + (wave * K_INSTR + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < V_INSTR; ++i)
+      dma16(vbase + (long)t0 * 2 + v_off[i], (lds_void*)(sb + K_BYTES + (wave * V_INSTR + i) * 1024));
+  };
+
+  const int t_first = (key_lo / KT) * KT;
+  const int ntiles = key_hi > t_first ? (key_hi - t_first + KT - 1) / KT : 0;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < ntiles) issue(t_first + s * KT, s);
 
 #pragma unroll 1
-  for (int t0 = (key_lo / KT) * KT; t0 < key_hi; t0 += KT) {
-    // stage K rows [t0, t0+KT) and V^T columns [t0, t0+KT); slots outside [key_lo, key_hi) read as 0
-    for (int c = tid; c < KT * DH / 8; c += 256) {
-      const int r = c / (DH / 8), cc = c - r * (DH / 8);
-      const int slot = t0 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (slot >= key_lo && slot < key_hi) v = *(const uint4*)(kbase + (long)slot * DH + cc * 8);
-      *(uint4*)&Ks[r * KLD + cc * 8] = v;
-    }
-    for (int c = tid; c < DH * KT / 8; c += 256) {
-      const int r = c / (KT / 8), cc = c - r * (KT / 8);
-      const int s0 = t0 + cc * 8;
-      const __bf16* src = vbase + (long)r * p.kv_cap + s0;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (s0 >= key_lo && s0 + 8 <= key_hi) {
-        v = *(const uint4*)src;
-      } else if (s0 + 8 > key_lo && s0 < key_hi) {
-        bf16x8 e;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = (s0 + i >= key_lo && s0 + i < key_hi) ? src[i] : (__bf16)0.f;
-        v = __builtin_bit_cast(uint4, e);
-      }
-      *(uint4*)&Vs[r * VLD + cc * 8] = v;
-    }
-    __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) wait_vmcnt<PER_TILE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (it + STAGES - 1 < ntiles) issue(t_first + (it + STAGES - 1) * KT, (it + STAGES - 1) % STAGES);
+    const int t0 = t_first + it * KT;
     if (wave_live && t0 < wave_lim) {
+      const char* sb = smem + (it % STAGES) * STAGE;
       f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) sc[kb][j] = 0.f;
+        const int r = kb * 32 + l32;
 #pragma unroll
         for (int s = 0; s < DH / 16; ++s) {
-          const bf16x8 a = *(const bf16x8*)&Ks[(kb * 32 + l32) * KLD + s * 16 + half * 8];
+          const int c = 2 * s + half;
+          const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+          const bf16x8 a = *(const bf16x8*)(sb + r * KROW + cs * 16);
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[kb], 0, 0, 0);
         }
 #pragma unroll
@@ -171,38 +209,36 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int db = 0; db < DH / 32; ++db) {
-            const __bf16* vr = &Vs[(db * 32 + l32) * VLD + kb * 32 + 16 * c + half * 4];
-            const bf16x4 lo = *(const bf16x4*)vr;
-            const bf16x4 hi = *(const bf16x4*)(vr + 8);
+            // keys kb*32 + 16c + 4*half + {0..3} and + 8: chunk 4kb + 2c (+1), byte 8*half
+            const int r = db * 32 + l32;
+            const int ch = 4 * kb + 2 * c;
+            const char* row = sb + K_BYTES + r * 128 + half * 8;
+            const bf16x4 lo = *(const bf16x4*)(row + ((ch ^ ((r >> 1) & 7)) << 4));
+            const bf16x4 hi = *(const bf16x4*)(row + (((ch + 1) ^ ((r >> 1) & 7)) << 4));
             const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][c], st.o[db], 0, 0, 0);
           }
     }
-    __syncthreads();
   }
 
   if (NS && wave_live) {
-    // the candidate's own NS keys: query g = c*P + k sees g' in [c*P, g]
+    // the candidate's own NS keys: query g = c*P + k sees g' in [c*P, g];
+    // NS K and V are row-major [H][nq][dh]
     const int P = p.P;
     const int g_lo = (wq0 / P) * P;
     const int g_hi = min(wq0 + 31, p.nq - 1);
     const int my_first = (qi / P) * P;
     const __bf16* knb = p.kn + h * p.kn_head_stride;
-    const __bf16* vnb = p.vtn + h * p.kn_head_stride;
+    const __bf16* vnb = p.vn + h * p.kn_head_stride;
 #pragma unroll 1
     for (int t0 = g_lo; t0 <= g_hi; t0 += 32) {
       f32x16 sc[1];
 #pragma unroll
       for (int j = 0; j < 16; ++j) sc[0][j] = 0.f;
-      const int krow = t0 + l32;
+      const int krow = min(t0 + l32, p.nq - 1);
 #pragma unroll
       for (int s = 0; s < DH / 16; ++s) {
-        bf16x8 a;
-        if (krow < p.nq) a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
-        else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) a[i] = (__bf16)0.f;
-        }
+        const bf16x8 a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
         sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[0], 0, 0, 0);
       }
 #pragma unroll
@@ -217,12 +253,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int db = 0; db < DH / 32; ++db) {
-          const __bf16* vr = vnb + (long)(db * 32 + l32) * p.nq;
           bf16x8 a;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const int key = t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2);
-            a[i] = key < p.nq ? vr[key] : (__bf16)0.f;
+            const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), p.nq - 1);
+            a[i] = vnb[(long)key * DH + db * 32 + l32];
           }
           st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][c], st.o[db], 0, 0, 0);
         }
@@ -248,10 +283,25 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   }
 }
 
+// Zero the K rows and V^T columns [from, cap) of every (user, head) block, so
+// that key tiles reaching past the filled length read finite values.
+__global__ void cache_clear_tail_kernel(__bf16* k, __bf16* vt, int blocks, int dh, int cap, int from) {
+  const int b = blockIdx.y;
+  const int n = cap - from;
+  __bf16* kb = k + (long)b * cap * dh;
+  __bf16* vb = vt + (long)b * dh * cap;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n * dh; i += gridDim.x * blockDim.x) {
+    kb[(long)from * dh + i] = (__bf16)0.f;
+    const int r = i / n, c = i - r * n;
+    vb[(long)r * cap + from + c] = (__bf16)0.f;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s) {
   if (p.nq <= 0 || n_seg <= 0) return hipSuccess;
+  if (p.kv_cap % KT != 0) return hipErrorInvalidValue;
   dim3 grid((p.nq + 127) / 128, p.H, n_seg);
   dim3 block(256);
   if (dh == 64) {
@@ -263,6 +313,15 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_clear_tail(__bf16* k, __bf16* vt, int blocks, int dh, int cap, int from, hipStream_t s) {
+  if (from >= cap || blocks <= 0) return hipSuccess;
+  const int n = (cap - from) * dh;
+  int gx = (n + 255) / 256;
+  if (gx > 64) gx = 64;
+  hipLaunchKernelGGL(cache_clear_tail_kernel, dim3(gx, blocks), dim3(256), 0, s, k, vt, blocks, dh, cap, from);
   return hipGetLastError();
 }
 

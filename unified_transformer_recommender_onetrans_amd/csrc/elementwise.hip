@@ -83,7 +83,45 @@ __global__ void cache_read_kernel(const __bf16* __restrict__ k, const __bf16* __
   }
 }
 
+// One wave per row: sum of squares over d (lane-strided, coalesced), wave
+// reduction, then the scaled row written as fp16.
+__global__ __launch_bounds__(256) void rmsnorm_f16_kernel(NormParams p) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int g = blockIdx.y;
+  if (row >= p.M) return;
+  const RowMap& rm = p.rm;
+  const int seg = row / rm.rows_per_seg, t = row - seg * rm.rows_per_seg;
+  const float* src = p.res + (long)seg * rm.res_seg_stride + (rm.res_row_base + t) * rm.res_row_stride +
+                     (long)g * rm.res_group_stride;
+  const float* gain = p.gain + (long)g * p.gain_group_stride;
+  _Float16* dst = p.out + (((long)seg * rm.rows_per_seg + t) * rm.row_mult + g) * p.d;
+  constexpr int MAXE = 16;  // d <= 1024
+  float v[MAXE];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXE; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < p.d ? src[c] : 0.f;
+    ss += v[i] * v[i];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float r = 1.0f / sqrtf(ss / (float)p.d + p.eps);
+#pragma unroll
+  for (int i = 0; i < MAXE; ++i) {
+    const int c = lane + 64 * i;
+    if (c < p.d) dst[c] = (_Float16)(v[i] * r * gain[c]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) {
+  if (p.M <= 0 || p.groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((p.M + 3) / 4, p.groups), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

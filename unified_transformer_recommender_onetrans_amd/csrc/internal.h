@@ -1,9 +1,78 @@
 // Internal interfaces between the C ABI layer and the gfx950 kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace onetrans {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Reads of LDS tiles that arrive by DMA. Written as inline asm because the
+// compiler cannot tell which DMA a plain LDS load depends on and would wait for
+// every DMA still in flight (draining the pipeline) before each read. Each asm
+// block issues its reads and waits for them (lgkmcnt(0)) before it ends, so no
+// output register is ever seen before its data has landed. Addresses are LDS
+// byte addresses.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void lds_read_b128x1(u32x4& o0, uint32_t a0) {
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(o0) : "v"(a0));
+}
+__device__ __forceinline__ void lds_read_b128x2(u32x4& o0, u32x4& o1, uint32_t a0, uint32_t a1) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(o0), "=&v"(o1) : "v"(a0), "v"(a1));
+}
+__device__ __forceinline__ void lds_read_b128x3(u32x4& o0, u32x4& o1, u32x4& o2, uint32_t a0, uint32_t a1,
+                                                uint32_t a2) {
+  asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(o0), "=&v"(o1), "=&v"(o2) : "v"(a0), "v"(a1), "v"(a2));
+}
+__device__ __forceinline__ void lds_read_b128x4(u32x4& o0, u32x4& o1, u32x4& o2, u32x4& o3, uint32_t a0,
+                                                uint32_t a1, uint32_t a2, uint32_t a3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3) : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
+}
+__device__ __forceinline__ void lds_read_b64x4(u32x2& o0, u32x2& o1, u32x2& o2, u32x2& o3, uint32_t a0,
+                                               uint32_t a1, uint32_t a2, uint32_t a3) {
+  asm volatile(
+      "ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3) : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
+}
+
+// GELU(x) = x/2 (1 + erf(x / sqrt 2)) with erf from Abramowitz & Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 for all
+// x): erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0.
+// About 14 VALU operations; its error is three orders of magnitude below the
+// fp16 rounding applied to the result.
+__device__ __forceinline__ float gelu_as(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float q = fmaf(1.061405429f, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  q *= t;
+  const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
+  const float erf_abs = fmaf(-q, e, 1.0f);
+  const float hx = 0.5f * x;
+  return fmaf(hx, __builtin_copysignf(erf_abs, x), hx);
+}
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's bytes land at lds + 16 * i. The 16-byte form exists only on gfx950, so the
+// host compilation pass, which never runs device code, does not see the builtin.
+__device__ __forceinline__ void dma16(const void* g, lds_void* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+#endif
+}
 
 // Row addressing shared by the GEMM prologue/epilogue.
 //
@@ -23,12 +92,8 @@ struct RowMap {
 struct GemmParams {
   int M, N, K, groups;
   RowMap rm;
-  // A operand: fp32 residual rows normalised by RMSNorm (norm mode), or fp16 hidden rows
-  const float* res_in;       // norm mode source (residual addressing)
-  const float* gain;         // [K] per group, stride gain_group_stride
-  long gain_group_stride;
-  float eps;
-  const _Float16* hid_in;    // plain mode source (hidden addressing, ld = K)
+  // A operand: fp16 rows at a_in + hidden_row * K (RMSNorm'd activations or FFN hidden rows)
+  const _Float16* a_in;
   // B operand: weights [N][K] (fp16 or E4M3FN codes), per-group stride in elements
   const void* w;
   long w_group_stride;
@@ -37,7 +102,9 @@ struct GemmParams {
   // epilogue: Q/K/V scatter
   int d, dh;
   __bf16* q; long q_seg_stride, q_head_stride; int q_from;
-  __bf16* k; __bf16* vt; long kv_seg_stride, kv_head_stride; int kv_cap, kv_slot_base;
+  // K rows [.][H][slots][dh]; V either transposed (vt: [.][H][dh][kv_cap], the S cache)
+  // or, when vt is NULL, row-major like K (v: the per-candidate NS values)
+  __bf16* k; __bf16* vt; __bf16* v; long kv_seg_stride, kv_head_stride; int kv_cap, kv_slot_base;
   // epilogue: GELU into hidden rows (ld = N)
   _Float16* hid_out;
   // epilogue: residual add (residual addressing)
@@ -46,7 +113,8 @@ struct GemmParams {
 
 enum GemmKind { GEMM_QKV = 0, GEMM_FFN_UP = 1, GEMM_FFN_DOWN = 2 };
 
-hipError_t launch_gemm(GemmKind kind, bool fp8_weights, const GemmParams& p, hipStream_t s);
+// ns selects the private-weight (NS) instance; fp8_weights only applies to it.
+hipError_t launch_gemm(GemmKind kind, bool fp8_weights, bool ns, const GemmParams& p, hipStream_t s);
 
 // Attention of `nq` queries per (seg, head) against a K/V block (cache layout:
 // K [.][H][cap][dh], V transposed [.][H][dh][cap]) plus, for NS queries, the
@@ -60,12 +128,48 @@ struct AttnParams {
   int key_pos0;      // global position of key slot 0
   int q_pos0;        // global position of query 0 (S queries: causal limit)
   const int* valid_from;   // [seg] first valid global position (NS: one value)
-  // NS only: own keys of the candidates, kn [H][nq][dh], vtn [H][dh][nq]; P NS tokens each
-  const __bf16* kn; const __bf16* vtn; long kn_head_stride; int P;
+  // NS only: own keys and values of the candidates, row-major kn, vn [H][nq][dh]; P NS tokens each
+  const __bf16* kn; const __bf16* vn; long kn_head_stride; int P;
   float scale_log2;  // log2(e) / sqrt(dh)
 };
 
 hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s);
+
+// Zeroes cache slots [from, cap) of `blocks` (user, head) blocks: K [blocks][cap][dh] and
+// V^T [blocks][dh][cap]. Key tiles that reach past the filled length then read zeros.
+hipError_t launch_cache_clear_tail(__bf16* k, __bf16* vt, int blocks, int dh, int cap, int from, hipStream_t s);
+
+// RMSNorm of M residual rows per group (residual addressing) into fp16 rows at
+// out + hidden_row * d, with the group's gain row: x / sqrt(mean(x^2) + eps) * g.
+struct NormParams {
+  int M, groups, d;
+  RowMap rm;
+  const float* res;
+  const float* gain;
+  long gain_group_stride;
+  float eps;
+  _Float16* out;
+};
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
+
+// Fused pre-norm FFN of the NS rows (one group per NS position):
+//   y = z + W2 GELU(W1 RMSNorm(z; gain)) in place on the residual rows, and, when
+//   next_xn is not NULL, next_xn = fp16 RMSNorm(y; next_gain) in hidden addressing.
+struct FfnParams {
+  int M, groups, d, F;
+  RowMap rm;
+  float* res;
+  const float* gain;          // [groups][d], stride gain_group_stride (also for next_gain)
+  long gain_group_stride;
+  float eps;
+  const void* w1; const void* w2;   // [groups][F][d], [groups][d][F]; fp16 or E4M3 codes
+  long w1_group_stride, w2_group_stride;  // elements
+  const float* wscale;        // E4M3 only: [group*5 + 3] (W1), [group*5 + 4] (W2)
+  const float* next_gain;
+  _Float16* next_xn;
+};
+bool ffn_fused_supported(int d, int F);
+hipError_t launch_ffn_fused(bool fp8, const FfnParams& p, hipStream_t s);
 
 // Elementwise helpers.
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, long n, hipStream_t s);

@@ -5,8 +5,9 @@
 #include <string.h>
 
 #include <string>
+#include <vector>
 
-#include "../../include/onetrans.h"
+#include "onetrans.h"
 #include "internal.h"
 
 using namespace onetrans;
@@ -104,28 +105,30 @@ size_t cache_layout(const Shape& s, int B, size_t* k_off, size_t* v_off) {
   return off;
 }
 
-struct PrefillWs { size_t x, q, hid, total; };
+struct PrefillWs { size_t x, q, xn, hid, total; };
 PrefillWs prefill_ws(const Shape& s, int B) {
   PrefillWs w;
   size_t off = 0;
   w.x = off; off = align_up(off + (size_t)B * s.s_len * s.d * 4);
   w.q = off; off = align_up(off + (size_t)B * s.H * s.q[0] * s.dh * 2);
+  w.xn = off; off = align_up(off + (size_t)B * s.s_len * s.d * 2);
   w.hid = off; off = align_up(off + (size_t)B * s.q[0] * s.F * 2);
   w.total = off;
   return w;
 }
 
-struct AppendWs { size_t q, hid, total; };
+struct AppendWs { size_t q, xn, hid, total; };
 AppendWs append_ws(const Shape& s, int B, int m) {
   AppendWs w;
   size_t off = 0;
   w.q = off; off = align_up(off + (size_t)B * s.H * m * s.dh * 2);
+  w.xn = off; off = align_up(off + (size_t)B * m * s.d * 2);
   w.hid = off; off = align_up(off + (size_t)B * m * s.F * 2);
   w.total = off;
   return w;
 }
 
-struct ScoreWs { size_t qn, kn, vn, hid, total; };
+struct ScoreWs { size_t qn, kn, vn, xn, hid, total; };
 ScoreWs score_ws(const Shape& s, int C) {
   ScoreWs w;
   size_t off = 0;
@@ -133,6 +136,7 @@ ScoreWs score_ws(const Shape& s, int C) {
   w.qn = off; off = align_up(off + rows * s.d * 2);
   w.kn = off; off = align_up(off + rows * s.d * 2);
   w.vn = off; off = align_up(off + rows * s.d * 2);
+  w.xn = off; off = align_up(off + rows * s.d * 2);
   w.hid = off; off = align_up(off + rows * s.F * 2);
   w.total = off;
   return w;
@@ -143,7 +147,7 @@ GemmParams base_gemm(const Shape& s) {
   memset(&g, 0, sizeof(g));
   g.d = s.d;
   g.dh = s.dh;
-  g.eps = s.eps;
+
   g.scale_col_div = 1 << 30;
   g.groups = 1;
   return g;
@@ -160,6 +164,44 @@ int hip_check(hipError_t e, const char* what) {
     if (rc_ != ONETRANS_OK) return rc_;         \
   } while (0)
 
+// ---- kernel timing diagnostics: HIP events around launches of selected families ----
+struct TimingRec {
+  int fam;
+  hipEvent_t a, b;
+};
+uint32_t g_timing_mask = 0;
+std::vector<TimingRec> g_timing;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct FamilyTimer {
+  int fam;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  FamilyTimer(int f, hipStream_t s) : fam(f), st(s) {
+    if (g_timing_mask & (1u << f)) {
+      a = pooled_event();
+      if (a && hipEventRecord(a, st) != hipSuccess) a = nullptr;
+    }
+  }
+  ~FamilyTimer() {
+    if (!a) return;
+    hipEvent_t b = pooled_event();
+    if (b && hipEventRecord(b, st) == hipSuccess) g_timing.push_back({fam, a, b});
+    else g_event_pool.push_back(a);
+  }
+};
+
 float scale_log2(const Shape& s) { return (float)(1.4426950408889634 / sqrt((double)s.dh)); }
 
 // ---- one S-side layer over `rows` rows per user (prefill: the layer input;
@@ -169,23 +211,38 @@ struct SLayerArgs {
   float* x; long x_seg_stride, x_row_base;  // residual rows of user u: x + u*x_seg_stride + (x_row_base + t)*d
   __bf16* k; __bf16* vt; int cap, slot_base, n_keys, key_pos0;
   const int* valid_from;
-  __bf16* qbuf; _Float16* hid;
+  __bf16* qbuf; _Float16* xn; _Float16* hid;
 };
+
+int run_norm(const Shape& s, int fam, int M, int groups, const RowMap& rm, const float* res, const float* gain,
+             long gain_group_stride, _Float16* out, hipStream_t st) {
+  NormParams np;
+  np.M = M; np.groups = groups; np.d = s.d; np.rm = rm; np.res = res; np.gain = gain;
+  np.gain_group_stride = gain_group_stride; np.eps = s.eps; np.out = out;
+  FamilyTimer t(fam, st);
+  OT_HIP(launch_rmsnorm(np, st), "RMSNorm launch");
+  return ONETRANS_OK;
+}
 
 int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SLayerArgs& a, hipStream_t st) {
   const long d = s.d;
   RowMap all{a.rows, 1, a.x_seg_stride, a.x_row_base, d, 0};
   RowMap tail{a.q, 1, a.x_seg_stride, a.x_row_base + (a.rows - a.q), d, 0};
 
+  int rc = run_norm(s, ONETRANS_K_S_NORM, a.B * a.rows, 1, all, a.x, (const float*)(pk + lo.s_ga), 0, a.xn, st);
+  if (rc) return rc;
   GemmParams g = base_gemm(s);
   g.M = a.B * a.rows; g.N = 3 * s.d; g.K = s.d;
   g.rm = all;
-  g.res_in = a.x; g.gain = (const float*)(pk + lo.s_ga);
+  g.a_in = a.xn;
   g.w = pk + lo.s_wqkv;
   g.q = a.qbuf; g.q_seg_stride = (long)s.H * a.q * s.dh; g.q_head_stride = (long)a.q * s.dh; g.q_from = a.rows - a.q;
   g.k = a.k; g.vt = a.vt; g.kv_seg_stride = (long)s.H * a.cap * s.dh; g.kv_head_stride = (long)a.cap * s.dh;
   g.kv_cap = a.cap; g.kv_slot_base = a.slot_base;
-  OT_HIP(launch_gemm(GEMM_QKV, false, g, st), "S QKV GEMM launch");
+  {
+    FamilyTimer t(ONETRANS_K_S_QKV, st);
+    OT_HIP(launch_gemm(GEMM_QKV, false, false, g, st), "S QKV GEMM launch");
+  }
 
   AttnParams at;
   memset(&at, 0, sizeof(at));
@@ -198,23 +255,34 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
   at.valid_from = a.valid_from;
   at.P = 1;
   at.scale_log2 = scale_log2(s);
-  OT_HIP(launch_attention(false, s.dh, at, a.B, st), "S attention launch");
+  {
+    FamilyTimer t(ONETRANS_K_S_ATTN, st);
+    OT_HIP(launch_attention(false, s.dh, at, a.B, st), "S attention launch");
+  }
 
+  rc = run_norm(s, ONETRANS_K_S_NORM, a.B * a.q, 1, tail, a.x, (const float*)(pk + lo.s_gf), 0, a.xn, st);
+  if (rc) return rc;
   GemmParams u = base_gemm(s);
   u.M = a.B * a.q; u.N = s.F; u.K = s.d;
   u.rm = tail;
-  u.res_in = a.x; u.gain = (const float*)(pk + lo.s_gf);
+  u.a_in = a.xn;
   u.w = pk + lo.s_w1;
   u.hid_out = a.hid;
-  OT_HIP(launch_gemm(GEMM_FFN_UP, false, u, st), "S FFN up launch");
+  {
+    FamilyTimer t(ONETRANS_K_S_FFN_UP, st);
+    OT_HIP(launch_gemm(GEMM_FFN_UP, false, false, u, st), "S FFN up launch");
+  }
 
   GemmParams dn = base_gemm(s);
   dn.M = a.B * a.q; dn.N = s.d; dn.K = s.F;
   dn.rm = tail;
-  dn.hid_in = a.hid;
+  dn.a_in = a.hid;
   dn.w = pk + lo.s_w2;
   dn.res_out = a.x;
-  OT_HIP(launch_gemm(GEMM_FFN_DOWN, false, dn, st), "S FFN down launch");
+  {
+    FamilyTimer t(ONETRANS_K_S_FFN_DOWN, st);
+    OT_HIP(launch_gemm(GEMM_FFN_DOWN, false, false, dn, st), "S FFN down launch");
+  }
   return ONETRANS_OK;
 }
 
@@ -226,23 +294,36 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
   __bf16* qn = (__bf16*)(ws + w.qn);
   __bf16* kn = (__bf16*)(ws + w.kn);
   __bf16* vn = (__bf16*)(ws + w.vn);
+  _Float16* xn = (_Float16*)(ws + w.xn);
   _Float16* hid = (_Float16*)(ws + w.hid);
   const long d = s.d, P = s.P, rows = (long)C * P;
   const int* vf = (const int*)cache_buf;
-  OT_HIP(launch_bf16_to_f32(ns_tokens, ns_out, rows * d, st), "NS input conversion launch");
+  {
+    FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
+    OT_HIP(launch_bf16_to_f32(ns_tokens, ns_out, rows * d, st), "NS input conversion launch");
+  }
   const RowMap rm{C, s.P, 0, 0, P * d, d};
+  const bool fused = ffn_fused_supported(s.d, s.F);
   for (int l = 0; l < s.L; ++l) {
     const long cap = s.cap[l];
     const int len = s.n[l] + n_appended;
+    if (l == 0 || !fused) {  // with the fused FFN, layer l-1 already wrote this layer's pre-norm
+      int rc = run_norm(s, ONETRANS_K_NS_NORM, C, s.P, rm, ns_out, (const float*)(pk + lo[l].ns_ga), d, xn, st);
+      if (rc) return rc;
+    }
     GemmParams g = base_gemm(s);
     g.M = C; g.N = 3 * s.d; g.K = s.d; g.groups = s.P;
     g.rm = rm;
-    g.res_in = ns_out; g.gain = (const float*)(pk + lo[l].ns_ga); g.gain_group_stride = d;
+    g.a_in = xn;
     g.w = pk + lo[l].ns_wqkv; g.w_group_stride = 3 * d * d;
     g.wscale = (const float*)(pk + lo[l].ns_scale); g.scale_idx0 = 0; g.scale_col_div = s.d;
     g.q = qn; g.q_seg_stride = 0; g.q_head_stride = rows * s.dh; g.q_from = 0;
-    g.k = kn; g.vt = vn; g.kv_seg_stride = 0; g.kv_head_stride = rows * s.dh; g.kv_cap = (int)rows; g.kv_slot_base = 0;
-    OT_HIP(launch_gemm(GEMM_QKV, s.fp8, g, st), "NS QKV GEMM launch");
+    g.k = kn; g.vt = nullptr; g.v = vn; g.kv_seg_stride = 0; g.kv_head_stride = rows * s.dh; g.kv_cap = (int)rows;
+    g.kv_slot_base = 0;
+    {
+      FamilyTimer t(ONETRANS_K_NS_QKV, st);
+      OT_HIP(launch_gemm(GEMM_QKV, s.fp8, true, g, st), "NS QKV GEMM launch");
+    }
 
     AttnParams at;
     memset(&at, 0, sizeof(at));
@@ -255,27 +336,52 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     at.kv_seg_stride = 0; at.kv_head_stride = cap * s.dh; at.kv_cap = (int)cap;
     at.n_keys = len; at.key_pos0 = s.s_len - s.n[l]; at.q_pos0 = 0;
     at.valid_from = vf + user;
-    at.kn = kn; at.vtn = vn; at.kn_head_stride = rows * s.dh; at.P = s.P;
+    at.kn = kn; at.vn = vn; at.kn_head_stride = rows * s.dh; at.P = s.P;
     at.scale_log2 = scale_log2(s);
-    OT_HIP(launch_attention(true, s.dh, at, 1, st), "NS attention launch");
+    {
+      FamilyTimer t(ONETRANS_K_NS_ATTN, st);
+      OT_HIP(launch_attention(true, s.dh, at, 1, st), "NS attention launch");
+    }
 
+    if (fused) {
+      FfnParams fp;
+      memset(&fp, 0, sizeof(fp));
+      fp.M = C; fp.groups = s.P; fp.d = s.d; fp.F = s.F; fp.rm = rm;
+      fp.res = ns_out; fp.gain = (const float*)(pk + lo[l].ns_gf); fp.gain_group_stride = d; fp.eps = s.eps;
+      fp.w1 = pk + lo[l].ns_w1; fp.w2 = pk + lo[l].ns_w2;
+      fp.w1_group_stride = (long)s.F * d; fp.w2_group_stride = d * s.F;
+      fp.wscale = (const float*)(pk + lo[l].ns_scale);
+      fp.next_gain = l + 1 < s.L ? (const float*)(pk + lo[l + 1].ns_ga) : nullptr;
+      fp.next_xn = l + 1 < s.L ? xn : nullptr;
+      FamilyTimer t(ONETRANS_K_NS_FFN, st);
+      OT_HIP(launch_ffn_fused(s.fp8, fp, st), "NS fused FFN launch");
+      continue;
+    }
+    int rc = run_norm(s, ONETRANS_K_NS_NORM, C, s.P, rm, ns_out, (const float*)(pk + lo[l].ns_gf), d, xn, st);
+    if (rc) return rc;
     GemmParams u = base_gemm(s);
     u.M = C; u.N = s.F; u.K = s.d; u.groups = s.P;
     u.rm = rm;
-    u.res_in = ns_out; u.gain = (const float*)(pk + lo[l].ns_gf); u.gain_group_stride = d;
+    u.a_in = xn;
     u.w = pk + lo[l].ns_w1; u.w_group_stride = (long)s.F * d;
     u.wscale = (const float*)(pk + lo[l].ns_scale); u.scale_idx0 = 3;
     u.hid_out = hid;
-    OT_HIP(launch_gemm(GEMM_FFN_UP, s.fp8, u, st), "NS FFN up launch");
+    {
+      FamilyTimer t(ONETRANS_K_NS_FFN_UP, st);
+      OT_HIP(launch_gemm(GEMM_FFN_UP, s.fp8, true, u, st), "NS FFN up launch");
+    }
 
     GemmParams dn = base_gemm(s);
     dn.M = C; dn.N = s.d; dn.K = s.F; dn.groups = s.P;
     dn.rm = rm;
-    dn.hid_in = hid;
+    dn.a_in = hid;
     dn.w = pk + lo[l].ns_w2; dn.w_group_stride = d * s.F;
     dn.wscale = (const float*)(pk + lo[l].ns_scale); dn.scale_idx0 = 4;
     dn.res_out = ns_out;
-    OT_HIP(launch_gemm(GEMM_FFN_DOWN, s.fp8, dn, st), "NS FFN down launch");
+    {
+      FamilyTimer t(ONETRANS_K_NS_FFN_DOWN, st);
+      OT_HIP(launch_gemm(GEMM_FFN_DOWN, s.fp8, true, dn, st), "NS FFN down launch");
+    }
   }
   (void)n_users;
   return ONETRANS_OK;
@@ -287,7 +393,16 @@ int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const u
   const PrefillWs w = prefill_ws(s, B);
   float* x = (float*)(ws + w.x);
   int* vf = (int*)cache_buf;
-  OT_HIP(launch_s_input(s_tokens, s_lens, x, vf, B, s.s_len, s.d, st), "S input conversion launch");
+  {
+    FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
+    OT_HIP(launch_s_input(s_tokens, s_lens, x, vf, B, s.s_len, s.d, st), "S input conversion launch");
+  }
+  for (int l = 0; l < s.L; ++l) {
+    FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
+    OT_HIP(launch_cache_clear_tail((__bf16*)(cache_buf + k_off[l]), (__bf16*)(cache_buf + v_off[l]), B * s.H, s.dh,
+                                   s.cap[l], s.n[l], st),
+           "cache tail clear launch");
+  }
   for (int l = 0; l < s.L; ++l) {
     SLayerArgs a;
     a.B = B; a.rows = s.n[l]; a.q = s.q[l];
@@ -295,14 +410,17 @@ int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const u
     a.k = (__bf16*)(cache_buf + k_off[l]); a.vt = (__bf16*)(cache_buf + v_off[l]);
     a.cap = s.cap[l]; a.slot_base = 0; a.n_keys = s.n[l]; a.key_pos0 = s.s_len - s.n[l];
     a.valid_from = vf;
-    a.qbuf = (__bf16*)(ws + w.q); a.hid = (_Float16*)(ws + w.hid);
+    a.qbuf = (__bf16*)(ws + w.q); a.xn = (_Float16*)(ws + w.xn); a.hid = (_Float16*)(ws + w.hid);
     int rc = run_s_layer(s, pk, lo[l], a, st);
     if (rc) return rc;
   }
   const int qL = s.q[s.L - 1];
-  OT_HIP(launch_copy_rows_f32(x + (long)(s.s_len - qL) * s.d, (long)s.s_len * s.d, s_out, (long)qL * s.d,
+  {
+    FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
+    OT_HIP(launch_copy_rows_f32(x + (long)(s.s_len - qL) * s.d, (long)s.s_len * s.d, s_out, (long)qL * s.d,
                               (long)qL * s.d, B, st),
          "S output copy launch");
+  }
   return ONETRANS_OK;
 }
 
@@ -476,7 +594,10 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
   cache_layout(s, B, k_off, v_off);
   char* cb = (char*)cache->buf;
   char* ws = (char*)workspace;
-  OT_HIP(launch_bf16_to_f32(new_tokens, new_out, (long)B * m * s.d, stream), "append input conversion launch");
+  {
+    FamilyTimer t(ONETRANS_K_ELEMENTWISE, stream);
+    OT_HIP(launch_bf16_to_f32(new_tokens, new_out, (long)B * m * s.d, stream), "append input conversion launch");
+  }
   for (int l = 0; l < s.L; ++l) {
     const int len = s.n[l] + cache->n_appended;
     SLayerArgs a;
@@ -485,7 +606,7 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
     a.k = (__bf16*)(cb + k_off[l]); a.vt = (__bf16*)(cb + v_off[l]);
     a.cap = s.cap[l]; a.slot_base = len; a.n_keys = len + m; a.key_pos0 = s.s_len - s.n[l];
     a.valid_from = (const int*)cb;
-    a.qbuf = (__bf16*)(ws + w.q); a.hid = (_Float16*)(ws + w.hid);
+    a.qbuf = (__bf16*)(ws + w.q); a.xn = (_Float16*)(ws + w.xn); a.hid = (_Float16*)(ws + w.hid);
     rc = run_s_layer(s, (const char*)packed, lo[l], a, stream);
     if (rc) return rc;
   }
@@ -567,6 +688,35 @@ int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* 
   OT_HIP(launch_cache_read((const __bf16*)(cb + k_off[layer]) + uo, (const __bf16*)(cb + v_off[layer]) + uo, s.H, s.dh,
                            s.cap[layer], rows, (__bf16*)k_out, (__bf16*)v_out, stream),
          "cache read launch");
+  return ONETRANS_OK;
+}
+
+int onetrans_kernel_timing_enable(uint32_t mask) {
+  for (const TimingRec& r : g_timing) {
+    (void)hipEventSynchronize(r.b);
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_timing.clear();
+  g_timing_mask = mask & ((1u << ONETRANS_K_COUNT) - 1);
+  return ONETRANS_OK;
+}
+
+int onetrans_kernel_timing_read(int family, double* total_ms, int64_t* launches) {
+  if (family < 0 || family >= ONETRANS_K_COUNT || !total_ms || !launches)
+    return fail(ONETRANS_ERR_INVALID_ARG, "bad kernel family or NULL output");
+  double sum = 0.0;
+  int64_t n = 0;
+  for (const TimingRec& r : g_timing) {
+    if (r.fam != family) continue;
+    OT_HIP(hipEventSynchronize(r.b), "event synchronize");
+    float ms = 0.f;
+    OT_HIP(hipEventElapsedTime(&ms, r.a, r.b), "event elapsed time");
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
   return ONETRANS_OK;
 }
 
