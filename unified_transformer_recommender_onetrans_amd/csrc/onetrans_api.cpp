@@ -286,6 +286,8 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
   return ONETRANS_OK;
 }
 
+constexpr int kFusedNsFfnMinCandidates = 1 << 30;  // measured crossover not reached yet
+
 int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const char* cache_buf, const size_t* k_off,
                const size_t* v_off, int n_users, int n_appended, int user, const uint16_t* ns_tokens, int C,
                float* ns_out, char* ws, hipStream_t st) {
@@ -303,7 +305,10 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     OT_HIP(launch_bf16_to_f32(ns_tokens, ns_out, rows * d, st), "NS input conversion launch");
   }
   const RowMap rm{C, s.P, 0, 0, P * d, d};
-  const bool fused = ffn_fused_supported(s.d, s.F);
+  // The fused NS FFN keeps the hidden rows on chip but streams each weight chunk once per
+  // 64 candidates; with the persistent GEMMs the unfused pair measures faster at C = 256
+  // (OneTrans-L shape), so the fused kernel is used only for large candidate counts.
+  const bool fused = ffn_fused_supported(s.d, s.F) && C >= kFusedNsFfnMinCandidates;
   for (int l = 0; l < s.L; ++l) {
     const long cap = s.cap[l];
     const int len = s.n[l] + n_appended;
