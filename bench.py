@@ -179,20 +179,71 @@ def timed(fn, steps, warmup, sync):
     return time.perf_counter() - t0
 
 
-def roofline_entry(family, flops, nbytes, ms, launches):
+# Source files whose text decides each kernel family's memory traffic.
+FAMILY_SOURCES = {
+    "s_qkv": "gemm.hip", "s_ffn_up": "gemm.hip", "s_ffn_down": "gemm.hip", "ns_qkv": "gemm.hip",
+    "ns_ffn_up": "gemm.hip", "ns_ffn_down": "gemm.hip", "s_attn": "attention.hip", "ns_attn": "attention.hip",
+    "ns_ffn": "ffn.hip", "s_norm": "elementwise.hip", "ns_norm": "elementwise.hip", "elementwise": "elementwise.hip",
+}
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "unified_transformer_recommender_onetrans_amd", "csrc")
+
+
+def source_digest(family: str) -> str:
+    """sha256 over the family's kernel source and the shared device header."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (FAMILY_SOURCES[family], "internal.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(family: str, workload: str):
+    """HBM bytes per launch from the committed counter summary (rocprofv3 FETCH_SIZE and WRITE_SIZE,
+    scaled by a copy kernel's calibration), or None when there is none or the kernel source changed
+    since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{workload}_{family}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("source_sha256") != source_digest(family):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def roofline_entry(family, flops, nbytes, ms, launches, traffic=None):
     sec = ms / 1e3
     intensity = flops / nbytes if nbytes else float("inf")
+    common = {"traffic": traffic, "launches": launches, "avg_launch_us": round(ms / launches * 1e3, 2),
+              "algorithmic_flops_per_launch": flops / launches, "algorithmic_bytes_per_launch": nbytes / launches}
     if intensity >= RIDGE:
         ach = flops / sec / 1e12
         return {"kernel": family, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_TFLOPS_16BIT,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS_16BIT, 4), "traffic": None,
-                "launches": launches, "avg_launch_us": round(ms / launches * 1e3, 2),
-                "algorithmic_flops_per_launch": flops / launches, "algorithmic_bytes_per_launch": nbytes / launches}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS_16BIT, 4), **common}
     ach = nbytes / sec / 1e9
     return {"kernel": family, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "launches": launches,
-            "avg_launch_us": round(ms / launches * 1e3, 2),
-            "algorithmic_flops_per_launch": flops / launches, "algorithmic_bytes_per_launch": nbytes / launches}
+            "frac": round(ach / PEAK_HBM_GBS, 4), **common}
+
+
+def copy_calibration(mib: int, reps: int) -> None:
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "reps": reps}))
 
 
 def cpu_baseline(wl, raw, s, lens, ns, budget_s: float):
@@ -231,7 +282,12 @@ def main():
     ap.add_argument("--no-sub", action="store_true", help="skip the prefill-batch / append / scoring-only parts")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--workload", default="onetrans_l", choices=["onetrans_l", "onetrans_s", "candidate_heavy_fp8"])
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib, 5)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the multi-GPU design is "
                                    "documented, not built)", "n_gpus": args.gpus}))
@@ -291,7 +347,8 @@ def main():
     ms_dom, n_dom = kernel_timing_read(dominant)
     kernel_timing_enable([])
     fl, by = work[dominant]
-    roof = roofline_entry(dominant, fl * args.steps, by * args.steps, ms_dom, n_dom)
+    roof = roofline_entry(dominant, fl * args.steps, by * args.steps, ms_dom, n_dom,
+                          measured_traffic(dominant, args.workload))
 
     ms_step = el / args.steps * 1e3
     tflops = step_flops / (el / args.steps) / 1e12

@@ -18,6 +18,8 @@ ARCH = "gfx950"
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
          # no packed-fp32 instructions: plain scalar fp32 code only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in ordinary VGPRs: no copies between AGPRs and VGPRs
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", INCLUDE, "-Wno-unused-result"]
 
 

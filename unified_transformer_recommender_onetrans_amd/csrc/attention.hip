@@ -46,15 +46,18 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int DH>
 struct Softmax {
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // running max (raw score units) and sum of this lane's query
   f32x16 o[DH / 32];
 };
 
-// Online-softmax update with NB 32-key blocks of scores already masked and
-// scaled into log2 units; returns the bf16 probabilities packed as the B
-// operands (keys 0-15 and 16-31 of each block in the lane's slot order).
+// Online-softmax update with NB 32-key blocks of raw scores (masked entries -inf).
+// The scale 1/sqrt(dh) * log2(e) is applied inside exp2 as one fma. The O
+// accumulators are rescaled only when some lane's running max grew: otherwise
+// the factor is exactly 1 and the multiply is skipped. Returns the bf16
+// probabilities packed as the B operands of the P.V product.
 template <int DH, int NB>
-__device__ __forceinline__ void softmax_update(Softmax<DH>& st, f32x16 (&sc)[NB], bf16x8 (&pb)[NB][2]) {
+__device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&sc)[NB], bf16x8 (&pb)[NB][2],
+                                               float scale) {
   float mt = -INFINITY;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -62,9 +65,16 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, f32x16 (&sc)[NB]
     for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sc[b][j]);
   mt = fmaxf(mt, __shfl_xor(mt, 32));
   const float m_new = fmaxf(st.m, mt);
-  const bool none = (m_new == -INFINITY);
-  const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(st.m - m_new);
-  const float msub = none ? 0.f : m_new;
+  if (__builtin_amdgcn_ballot_w64(m_new > st.m) != 0) {
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((st.m - m_new) * scale);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[db][j] *= alpha;
+    st.m = m_new;
+  }
+  const float msub = st.m == -INFINITY ? 0.f : -st.m * scale;
   float ps = 0.f;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -72,26 +82,22 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, f32x16 (&sc)[NB]
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(sc[b][8 * c + i] - msub);
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[b][8 * c + i], scale, msub));
         ps += pv;
         pb[b][c][i] = (__bf16)pv;
       }
-  st.l = st.l * alpha + ps;
-  st.m = m_new;
-#pragma unroll
-  for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) st.o[db][j] *= alpha;
+  st.l += ps;
 }
 
-template <int DH, bool NS>
-__global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+template <int DH, bool NS, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   constexpr int KROW = DH * 2;                // bytes per K row (64 or 128)
   constexpr int K_BYTES = KT * KROW;
   constexpr int V_BYTES = DH * KT * 2;        // DH rows of 64 keys (128 B)
   constexpr int STAGE = K_BYTES + V_BYTES;
-  constexpr int K_INSTR = K_BYTES / 1024 / 4;
-  constexpr int V_INSTR = V_BYTES / 1024 / 4;
+  constexpr int K_INSTR = K_BYTES / 1024 / NW;  // DMA instructions per wave and tile
+  constexpr int V_INSTR = V_BYTES / 1024 / NW;
+  static_assert(K_INSTR >= 1 && V_INSTR >= 1 && K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0, "tile split");
   constexpr int PER_TILE = K_INSTR + V_INSTR;
   constexpr int KCH = KROW / 16;              // 16-byte chunks per K row
   constexpr int KRPI = 64 / KCH;              // K rows per wave instruction
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y, seg = blockIdx.z;
-  const int wq0 = blockIdx.x * 128 + wave * 32;
+  const int wq0 = blockIdx.x * (NW * 32) + wave * 32;
   const int qi = wq0 + l32;
   const bool q_ok = qi < p.nq;
   const bool wave_live = wq0 < p.nq;
@@ -125,14 +131,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   int key_hi = p.n_keys;   // exclusive slot bound of the tiles this workgroup loads
   int my_lim = p.n_keys;   // exclusive slot bound of this lane's query
   int wave_lim = p.n_keys; // exclusive slot bound of this wave's queries
+  int wave_lim_lo = p.n_keys;  // smallest bound among them: tiles below it need no upper mask
   if (!NS) {
-    const int qlast_blk = min((int)blockIdx.x * 128 + 127, p.nq - 1);
+    const int qlast_blk = min((int)blockIdx.x * (NW * 32) + NW * 32 - 1, p.nq - 1);
     const int qlast_wave = min(wq0 + 31, p.nq - 1);
     key_hi = min(key_hi, p.q_pos0 + qlast_blk - p.key_pos0 + 1);
     wave_lim = min(wave_lim, p.q_pos0 + qlast_wave - p.key_pos0 + 1);
+    wave_lim_lo = min(wave_lim_lo, p.q_pos0 + wq0 - p.key_pos0 + 1);
     my_lim = min(my_lim, p.q_pos0 + qi - p.key_pos0 + 1);
   }
   if (!q_ok) my_lim = 0;
+  if (wq0 + 31 >= p.nq) wave_lim_lo = 0;  // a partial wave: some lanes see no keys
 
   Softmax<DH> st;
 #pragma unroll
@@ -194,15 +203,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
           const bf16x8 a = *(const bf16x8*)(sb + r * KROW + cs * 16);
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[kb], 0, 0, 0);
         }
+      }
+      if (t0 < key_lo || t0 + KT > wave_lim_lo) {  // a mask boundary falls inside this tile
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int slot = t0 + kb * 32 + 8 * (j >> 2) + half * 4 + (j & 3);
-          const bool vis = slot >= key_lo && slot < my_lim;
-          sc[kb][j] = vis ? sc[kb][j] * p.scale_log2 : -INFINITY;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int slot = t0 + kb * 32 + 8 * (j >> 2) + half * 4 + (j & 3);
+            if (slot < key_lo || slot >= my_lim) sc[kb][j] = -INFINITY;
+          }
       }
       bf16x8 pb[2][2];
-      softmax_update<DH, 2>(st, sc, pb);
+      softmax_update<DH, 2>(st, sc, pb, p.scale_log2);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -245,10 +257,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
       for (int j = 0; j < 16; ++j) {
         const int key = t0 + 8 * (j >> 2) + half * 4 + (j & 3);
         const bool vis = q_ok && key <= qi && key >= my_first;
-        sc[0][j] = vis ? sc[0][j] * p.scale_log2 : -INFINITY;
+        if (!vis) sc[0][j] = -INFINITY;
       }
       bf16x8 pb[1][2];
-      softmax_update<DH, 1>(st, sc, pb);
+      softmax_update<DH, 1>(st, sc, pb, p.scale_log2);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -299,20 +311,23 @@ __global__ void cache_clear_tail_kernel(__bf16* k, __bf16* vt, int blocks, int d
 
 }  // namespace
 
+template <int NW>
+void launch_attn_nw(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s) {
+  dim3 grid((p.nq + NW * 32 - 1) / (NW * 32), p.H, n_seg);
+  dim3 block(NW * 64);
+  if (dh == 64) {
+    if (ns) hipLaunchKernelGGL((attn_kernel<64, true, NW>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_kernel<64, false, NW>), grid, block, 0, s, p);
+  } else {
+    if (ns) hipLaunchKernelGGL((attn_kernel<32, true, NW>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_kernel<32, false, NW>), grid, block, 0, s, p);
+  }
+}
+
 hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s) {
   if (p.nq <= 0 || n_seg <= 0) return hipSuccess;
-  if (p.kv_cap % KT != 0) return hipErrorInvalidValue;
-  dim3 grid((p.nq + 127) / 128, p.H, n_seg);
-  dim3 block(256);
-  if (dh == 64) {
-    if (ns) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, s, p);
-  } else if (dh == 32) {
-    if (ns) hipLaunchKernelGGL((attn_kernel<32, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_kernel<32, false>), grid, block, 0, s, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (p.kv_cap % KT != 0 || (dh != 32 && dh != 64)) return hipErrorInvalidValue;
+  launch_attn_nw<4>(ns, dh, p, n_seg, s);
   return hipGetLastError();
 }
 

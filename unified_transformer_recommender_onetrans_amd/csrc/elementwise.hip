@@ -115,11 +115,59 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(NormParams p) {
   }
 }
 
+// Two rows per wave (32 lanes each), NV float4 per lane (d = 128 * NV): 16-byte loads,
+// a 32-lane reduction and 8-byte fp16 stores. Flattened row f = row * groups + group,
+// so consecutive waves walk memory in order for candidate-major NS rows.
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_f16_v4_kernel(NormParams p) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31;
+  const long f = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  if (f >= (long)p.M * p.groups) return;  // the two halves never exchange data
+  const int row = (int)(f / p.groups), g = (int)(f - (long)row * p.groups);
+  const RowMap& rm = p.rm;
+  const int seg = row / rm.rows_per_seg, t = row - seg * rm.rows_per_seg;
+  const float4* src = (const float4*)(p.res + (long)seg * rm.res_seg_stride + (rm.res_row_base + t) * rm.res_row_stride +
+                                      (long)g * rm.res_group_stride);
+  const float4* gain = (const float4*)(p.gain + (long)g * p.gain_group_stride);
+  _Float16* dst = p.out + (((long)seg * rm.rows_per_seg + t) * rm.row_mult + g) * p.d;
+  float4 v[NV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = src[l32 + 32 * i];
+    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  }
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float r = 1.0f / sqrtf(ss / (float)p.d + p.eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float4 gv = gain[l32 + 32 * i];
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 o = {(_Float16)(v[i].x * r * gv.x), (_Float16)(v[i].y * r * gv.y), (_Float16)(v[i].z * r * gv.z),
+                     (_Float16)(v[i].w * r * gv.w)};
+    *(f16x4*)(dst + 4 * (l32 + 32 * i)) = o;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) {
   if (p.M <= 0 || p.groups <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((p.M + 3) / 4, p.groups), dim3(256), 0, s, p);
+  const long rows = (long)p.M * p.groups;
+  const dim3 grid((unsigned)((rows + 7) / 8));
+  switch (p.d % 128 == 0 ? p.d / 128 : 0) {
+    case 1: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<1>, grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<2>, grid, dim3(256), 0, s, p); break;
+    case 3: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<3>, grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<4>, grid, dim3(256), 0, s, p); break;
+    case 5: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<5>, grid, dim3(256), 0, s, p); break;
+    case 6: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<6>, grid, dim3(256), 0, s, p); break;
+    case 7: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<7>, grid, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<8>, grid, dim3(256), 0, s, p); break;
+    default:  // d not a multiple of 128: one row per wave
+      hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((p.M + 3) / 4, p.groups), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -10,28 +10,30 @@
 //                   epilogue adds into the fp32 residual rows in place
 // A group is one NS position (private weights) or the shared S weights.
 //
-// Persistent schedule. The work list (BM x BN output tiles of every group) is
-// split into 8 contiguous ranges, one per XCD (the hardware dispatches block L to
-// XCD L % 8), and each XCD's workgroups take its items round-robin, so the
-// workgroups of one XCD work on neighbouring tiles that share weight rows and
-// activation rows in that XCD's L2. Each workgroup keeps STAGES-1 k-tiles in
-// flight across item boundaries: the next item's first tiles stream in while
-// the current item finishes, and its epilogue writes straight from the
-// accumulators, so the operand ring never drains.
+// Persistent schedule, one workgroup of 8 waves per CU. The work list (BM x BN
+// output tiles of every group) is split into 8 contiguous ranges, one per XCD
+// (the hardware dispatches block L to XCD L % 8), and each XCD's workgroups take
+// its items round-robin, so neighbouring tiles that share weight rows and
+// activation rows run together in that XCD's L2.
 //
-// Two workgroups share a CU (LDS <= 80 KB and <= 256 registers per lane each), so
-// one workgroup's epilogue (GELU, format conversion, stores) overlaps the other's
-// MFMA loop.
+// Warp specialisation. Loads and stores share one vmcnt counter on gfx9, so a
+// wave that both streams operands and writes results must wait for its own
+// stores whenever it waits for a k-tile. Here waves 4-7 only stream: they issue
+// the k-tiles (global -> LDS with global_load_lds_dwordx4, 16 bytes per lane),
+// wait for them and meet the compute waves at one barrier per k-tile. Waves 0-3
+// only compute: MFMA from LDS, then the epilogue's stores, which drain in the
+// background while the loaders keep up to STAGES-1 k-tiles of the next item in
+// flight. The ring holds 3-8 stages (about 128-144 KB of LDS).
 //
-// Data movement: k-tiles go global -> LDS with global_load_lds_dwordx4 (16 bytes
-// per lane, 1 KB per wave instruction). LDS rows are 64 or 128 bytes with their
-// 16-byte chunks XOR-swizzled by row, which keeps the MFMA fragment reads free of
-// bank conflicts on the 64-bank LDS.
+// LDS rows are 128 bytes (64 halfs of k) or 64 bytes (64 E4M3 codes) with their
+// 16-byte chunks XOR-swizzled by row, so the MFMA fragment reads are free of bank
+// conflicts on the 64-bank LDS.
 //
-// MFMA: v_mfma_f32_32x32x16_f16, 4 waves in a 2 x 2 grid, each owning a
-// (BM/2) x (BN/2) block of 32x32 accumulators. A lane ends up holding one output
-// column and groups of four consecutive rows, so each epilogue store instruction
-// writes 32 consecutive columns (64 or 128 contiguous bytes) of two rows.
+// MFMA: v_mfma_f32_32x32x16_f16; the compute waves form a WM x (4/WM) grid, each
+// owning a block of 32x32 accumulators. A lane ends up holding one output column
+// and groups of four consecutive rows, so each epilogue store instruction writes
+// 32 consecutive columns (64 or 128 contiguous bytes) of two rows. E4M3 weights
+// are decoded to fp16 exactly in registers after the LDS read.
 #include "internal.h"
 
 namespace onetrans {
@@ -129,23 +131,32 @@ __device__ __forceinline__ int swz(int c, int r) {
 }
 
 // SIDE (0 = shared S weights, 1 = private NS weights) only names the instance.
-template <int KIND, bool FP8, int SIDE, int BM, int BN, int BK, int STAGES, int WPC>
-__global__ __launch_bounds__(256, WPC) void gemm_kernel(GemmParams p, int n_tiles_m, int n_tiles_n, int n_items) {
-  constexpr int MI = BM / 64, NI = BN / 64;  // 32x32 blocks per wave
+// Waves 0-3 compute (a WM x (4/WM) grid over the tile), waves 4-7 load.
+template <int KIND, bool FP8, int SIDE, int BM, int BN, int STAGES, int WM>
+__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_m, int n_tiles_n, int n_items) {
+  constexpr int BK = 64;
+  constexpr int WN = 4 / WM;
+  constexpr int TM = BM / WM, TN = BN / WN;  // one compute wave's part of the tile
+  constexpr int MI = TM / 32, NI = TN / 32;  // 32x32 blocks per compute wave
   constexpr int AROW = BK * 2;               // bytes per LDS row: fp16 activations
   constexpr int BROW = FP8 ? BK : BK * 2;    // E4M3 codes or fp16 weights
   constexpr int A_BYTES = BM * AROW, B_BYTES = BN * BROW, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_INSTR = A_BYTES / 4096, B_INSTR = B_BYTES / 4096;  // per wave and k-tile
+  constexpr int A_INSTR = A_BYTES / 4096, B_INSTR = B_BYTES / 4096;  // per loader wave and k-tile
   constexpr int PT = A_INSTR + B_INSTR;
   constexpr int A_RPI = 1024 / AROW, B_RPI = 1024 / BROW;  // rows per DMA instruction
   constexpr int A_CPR = AROW / 16, B_CPR = BROW / 16;      // 16-byte chunks per row
+  static_assert(WM * WN == 4 && TM % 32 == 0 && TN % 32 == 0, "wave grid");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "tile shape");
-  static_assert(STAGES * STAGE <= 160 * 1024 / WPC, "LDS of WPC workgroups per CU");
-  static_assert(!FP8 || BROW == 64, "E4M3 tiles use 64-byte rows");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  // wave-private output staging (16-bit outputs): TM rows of TN values, rows padded by 16 bytes
+  constexpr bool STAGED = KIND != GEMM_FFN_DOWN;
+  constexpr int SP = TN * 2 + 16;                       // staging row pitch in bytes
+  constexpr int WSTG = STAGED ? TM * SP : 0;            // per compute wave
+  static_assert(STAGES >= 2 && STAGES * STAGE + 4 * WSTG <= 159 * 1024, "LDS");
+  static_assert(PT * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(TM * (TN / 8) % 64 == 0, "staged chunks per lane");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE + 4 * WSTG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const RowMap rm = p.rm;
   const int M = p.M, N = p.N, K = p.K;
   const float inv_rps = 1.0f / (float)rm.rows_per_seg;
@@ -161,46 +172,55 @@ __global__ __launch_bounds__(256, WPC) void gemm_kernel(GemmParams p, int n_tile
   const int my_items = jx < cnt ? (cnt - jx + nx - 1) / nx : 0;
   const int total_steps = my_items * nk;
 
-  // ---- issue side: per-lane sources of the direct-to-LDS loads for the item being fetched ----
-  const char* a_src[A_INSTR];
-  const char* b_src[B_INSTR];
-  int iss_t = 0, iss_kt = 0;  // item and k-tile of the next step to issue
-  auto set_sources = [&](int t) {
-    const int w = ib + t * nx;
-    const int mt = w % n_tiles_m, nt = (w / n_tiles_m) % n_tiles_n, g = w / (n_tiles_m * n_tiles_n);
-    const int m0 = mt * BM, n0 = nt * BN;
+  if (wave >= 4) {
+    // ================= loader waves: the only waves that touch vmcnt for operands =================
+    const int lw = wave - 4;
+    const char* a_src[A_INSTR];
+    const char* b_src[B_INSTR];
+    int iss_t = 0, iss_kt = 0;  // item and k-tile of the next step to issue
+    auto issue = [&](int s) {
+      if (iss_kt == 0) {
+        const int w = ib + iss_t * nx;
+        const int mt = w % n_tiles_m, nt = (w / n_tiles_m) % n_tiles_n, g = w / (n_tiles_m * n_tiles_n);
+        const int m0 = mt * BM, n0 = nt * BN;
 #pragma unroll
-    for (int i = 0; i < A_INSTR; ++i) {
-      const int r = (wave * A_INSTR + i) * A_RPI + lane / A_CPR;
-      const int row = min(m0 + r, M - 1);
-      int seg, tt;
-      split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
-      a_src[i] = (const char*)(p.a_in + hid_row(rm, seg, tt, g) * (long)K) + (swz<AROW>(lane % A_CPR, r) << 4);
+        for (int i = 0; i < A_INSTR; ++i) {
+          const int r = (lw * A_INSTR + i) * A_RPI + lane / A_CPR;
+          const int row = min(m0 + r, M - 1);
+          int seg, tt;
+          split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
+          a_src[i] = (const char*)(p.a_in + hid_row(rm, seg, tt, g) * (long)K) + (swz<AROW>(lane % A_CPR, r) << 4);
+        }
+        const char* wbase = (const char*)p.w + (long)g * p.w_group_stride * (FP8 ? 1 : 2);
+#pragma unroll
+        for (int i = 0; i < B_INSTR; ++i) {
+          const int r = (lw * B_INSTR + i) * B_RPI + lane / B_CPR;
+          const int n = min(n0 + r, N - 1);
+          b_src[i] = wbase + (long)n * K * (FP8 ? 1 : 2) + (swz<BROW>(lane % B_CPR, r) << 4);
+        }
+      }
+      char* st = smem + (s % STAGES) * STAGE;
+#pragma unroll
+      for (int i = 0; i < A_INSTR; ++i)
+        dma16(a_src[i] + iss_kt * AROW, (lds_void*)(st + (lw * A_INSTR + i) * 1024));
+#pragma unroll
+      for (int i = 0; i < B_INSTR; ++i)
+        dma16(b_src[i] + iss_kt * BROW, (lds_void*)(st + A_BYTES + (lw * B_INSTR + i) * 1024));
+      if (++iss_kt == nk) { iss_kt = 0; ++iss_t; }
+    };
+    int s_issue = 0;
+    for (; s_issue < STAGES - 1 && s_issue < total_steps; ++s_issue) issue(s_issue);
+#pragma unroll 1
+    for (int s = 0; s < total_steps; ++s) {
+      wait_tiles<PT, STAGES - 2>(s_issue - 1 - s);  // this wave's part of step s is in LDS
+      lds_barrier();                                // everyone's part is in; step s-1's stage is free
+      if (s_issue < total_steps) { issue(s_issue); ++s_issue; }
     }
-    const char* wbase = (const char*)p.w + (long)g * p.w_group_stride * (FP8 ? 1 : 2);
-#pragma unroll
-    for (int i = 0; i < B_INSTR; ++i) {
-      const int r = (wave * B_INSTR + i) * B_RPI + lane / B_CPR;
-      const int n = min(n0 + r, N - 1);
-      b_src[i] = wbase + (long)n * K * (FP8 ? 1 : 2) + (swz<BROW>(lane % B_CPR, r) << 4);
-    }
-  };
-  auto issue = [&](int s) {
-    if (iss_kt == 0) set_sources(iss_t);
-    char* st = smem + (s % STAGES) * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_INSTR; ++i)
-      dma16(a_src[i] + iss_kt * AROW, (lds_void*)(st + (wave * A_INSTR + i) * 1024));
-#pragma unroll
-    for (int i = 0; i < B_INSTR; ++i)
-      dma16(b_src[i] + iss_kt * BROW, (lds_void*)(st + A_BYTES + (wave * B_INSTR + i) * 1024));
-    if (++iss_kt == nk) { iss_kt = 0; ++iss_t; }
-  };
+    return;
+  }
 
-  int s_issue = 0;
-  for (; s_issue < STAGES - 1 && s_issue < total_steps; ++s_issue) issue(s_issue);
-  int landed = 0;  // steps below this are known to be in LDS
-
+  // ================= compute waves: MFMA and epilogue stores, never wait for operand loads =================
+  const int wm = wave / WN, wn = wave % WN;
 #pragma unroll 1
   for (int t = 0; t < my_items; ++t) {
     f32x16 acc[MI][NI];
@@ -214,9 +234,7 @@ __global__ __launch_bounds__(256, WPC) void gemm_kernel(GemmParams p, int n_tile
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
       const int s = t * nk + kt;
-      if (s >= landed) wait_tiles<PT, STAGES - 2>(s_issue - 1 - s);
-      lds_barrier();  // all waves' parts of step s are in; step s-1's stage is free
-      if (s_issue < total_steps) { issue(s_issue); ++s_issue; }
+      lds_barrier();  // step s is in LDS
       const char* st = smem + (s % STAGES) * STAGE;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
@@ -224,12 +242,12 @@ __global__ __launch_bounds__(256, WPC) void gemm_kernel(GemmParams p, int n_tile
         const int c = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          const int r = wm * (BM / 2) + mi * 32 + (lane & 31);
+          const int r = wm * TM + mi * 32 + (lane & 31);
           a[mi] = *(const f16x8*)(st + r * AROW + (swz<AROW>(c, r) << 4));
         }
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          const int r = wn * (BN / 2) + ni * 32 + (lane & 31);
+          const int r = wn * TN + ni * 32 + (lane & 31);
           if (FP8)
             b[ni] = e4m3x8_to_f16(*(const uint2*)(st + A_BYTES + r * 64 + (swz<64>(ks, r) << 4) + (lane >> 5) * 8));
           else
@@ -239,200 +257,238 @@ __global__ __launch_bounds__(256, WPC) void gemm_kernel(GemmParams p, int n_tile
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = STAGED ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b[ni], a[mi], acc[mi][ni], 0, 0, 0)
+                                 : __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
       }
     }
 
     // ---- epilogue. Lane holds column (lane % 32) of each 32x32 block and, in
     // registers 4q..4q+3, rows 8q + 4*(lane/32) + 0..3: a store instruction covers
-    // 32 consecutive columns of two rows ----
+    // 32 consecutive columns of two rows. Addresses: one base per group of four rows,
+    // then a constant step per row (integer multiplies run at a quarter of the VALU rate).
     const int w = ib + t * nx;
     const int mt = w % n_tiles_m, nt = (w / n_tiles_m) % n_tiles_n, g = w / (n_tiles_m * n_tiles_n);
     const int m0 = mt * BM, n0 = nt * BN;
     const float scale = FP8 ? p.wscale[g * 5 + p.scale_idx0 + n0 / p.scale_col_div] : 1.f;
-    const int col0 = n0 + wn * (BN / 2) + (lane & 31);     // + ni*32
-    const int row_w = m0 + wm * (BM / 2) + 4 * (lane >> 5);  // + mi*32 + 8q + e
-    const int rps = rm.rows_per_seg;
-    // row r = row_w + mi*32 + 8q + e  ->  (seg, t) of its first row, then step within the group
-    auto group_start = [&](int r0, int& seg, int& tt) { split_row(r0, rps, inv_rps, seg, tt); };
+    const int col0 = n0 + wn * TN + (lane & 31);     // + ni*32
+    const int row_w = m0 + wm * TM + 4 * (lane >> 5);  // + mi*32 + 8q + e
+    const int rps = rm.rows_per_seg, rmult = rm.row_mult;
     auto step = [&](int& seg, int& tt) {
       if (++tt >= rps) { tt = 0; ++seg; }
     };
-    if (KIND == GEMM_FFN_DOWN) {
-      float old[MI][4][4][NI];
+    // visits the (up to) four rows r0..r0+3 of one register group: f(element offset, e, t)
+    auto rows4 = [&](int r0, long rstep, auto&& base_of, auto&& f) {
+      int seg, tt;
+      split_row(r0, rps, inv_rps, seg, tt);
+      if (r0 + 3 < M && tt + 3 < rps) {
+        const long o = base_of(seg, tt);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+        for (int e = 0; e < 4; ++e) f(o + e * rstep, e, tt + e);
+      } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int seg, tt;
-          group_start(min(row_w + mi * 32 + 8 * q, M - 1), seg, tt);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float* src = p.res_out + res_row_off(rm, seg, tt, g) + col0;
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) old[mi][q][e][ni] = src[ni * 32];
-            if (row_w + mi * 32 + 8 * q + e + 1 < M) step(seg, tt);
-          }
+        for (int e = 0; e < 4; ++e) {
+          if (r0 + e >= M) break;
+          f(base_of(seg, tt), e, tt);
+          step(seg, tt);
         }
-      wait_vmcnt<0>();
-      landed = s_issue;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r0 = row_w + mi * 32 + 8 * q;
-          if (r0 >= M) continue;
-          int seg, tt;
-          group_start(r0, seg, tt);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (r0 + e >= M) break;
-            float* dst = p.res_out + res_row_off(rm, seg, tt, g) + col0;
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) dst[ni * 32] = old[mi][q][e][ni] + acc[mi][ni][4 * q + e] * scale;
-            step(seg, tt);
-          }
-        }
-    } else if (KIND == GEMM_FFN_UP) {
-      wait_vmcnt<0>();
-      landed = s_issue;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r0 = row_w + mi * 32 + 8 * q;
-          if (r0 >= M) continue;
-          int seg, tt;
-          group_start(r0, seg, tt);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (r0 + e >= M) break;
-            _Float16* dst = p.hid_out + hid_row(rm, seg, tt, g) * N + col0;
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) dst[ni * 32] = (_Float16)gelu_as(acc[mi][ni][4 * q + e] * scale);
-            step(seg, tt);
-          }
-        }
-    } else {
-      wait_vmcnt<0>();
-      landed = s_issue;
-      // BN divides d, so the whole tile lies in one of Q, K, V
-      const int typ = n0 / p.d;
-      const int dsh = p.dh == 64 ? 6 : 5;
-      long cofs[NI];  // per lane: head and in-head offset of its column in each block
-      int cjj[NI], chead[NI];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int c = col0 + ni * 32 - typ * p.d;
-        chead[ni] = c >> dsh;
-        cjj[ni] = c & (p.dh - 1);
-        cofs[ni] = (long)chead[ni] * (typ == 0 ? p.q_head_stride : p.kv_head_stride) + cjj[ni];
       }
-      const bool vt_mode = typ == 2 && p.vt != nullptr;
+    };
+    if (KIND == GEMM_FFN_DOWN) {
+      // read-modify-write of the fp32 residual, one 32-row block at a time to bound registers
+      auto base_of = [&](int seg, int tt) { return res_row_off(rm, seg, tt, g) + col0; };
+      const long rstep = rm.res_row_stride;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        float old[4][4][NI];
+        long off[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r0 = min(row_w + mi * 32 + 8 * q, M - 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) off[q][e] = -1;
+          rows4(r0, rstep, base_of, [&](long o, int e, int) { off[q][e] = o; });
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float* src = p.res_out + (off[q][e] >= 0 ? off[q][e] : off[q][0]);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) old[q][e][ni] = src[ni * 32];
+          }
+        }
+        wait_vmcnt<0>();  // the residual rows (and this wave's earlier stores)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (row_w + mi * 32 + 8 * q >= M) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (off[q][e] < 0 || row_w + mi * 32 + 8 * q + e >= M) continue;
+            float* dst = p.res_out + off[q][e];
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) dst[ni * 32] = old[q][e][ni] + acc[mi][ni][4 * q + e] * scale;
+          }
+        }
+      }
+    } else {
+      // ---- staged epilogue (Q / K / V and the GELU hidden rows). With the weight fragment
+      // first, lane holds output row (lane % 32) of each 32x32 block and, in registers
+      // 4q..4q+3, columns 8q + 4*(lane/32) + 0..3. They go to this wave's LDS staging rows
+      // (8 bytes per write), come back as 16-byte row chunks and leave as 16-byte stores. ----
+      char* stg = smem + STAGES * STAGE + wave * WSTG;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r0 = row_w + mi * 32 + 8 * q;
-          if (r0 >= M) continue;
-          int seg, tt;
-          group_start(r0, seg, tt);
-          if (vt_mode) {
-            // transposed V: the four rows of the group are four key slots of one column
-            const long ki = p.kv_slot_base + (long)tt * rm.row_mult + g;
-            if (rm.row_mult == 1 && r0 + 3 < M && tt + 3 < rps && (ki & 3) == 0) {
+        for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-              for (int ni = 0; ni < NI; ++ni) {
-                const bf16x4 o = {(__bf16)(acc[mi][ni][4 * q] * scale), (__bf16)(acc[mi][ni][4 * q + 1] * scale),
-                                  (__bf16)(acc[mi][ni][4 * q + 2] * scale), (__bf16)(acc[mi][ni][4 * q + 3] * scale)};
-                *(bf16x4*)(p.vt + seg * p.kv_seg_stride + chead[ni] * p.kv_head_stride + (long)cjj[ni] * p.kv_cap + ki) = o;
-              }
-              continue;
-            }
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (r0 + e >= M) break;
-              const long k1 = p.kv_slot_base + (long)tt * rm.row_mult + g;
-#pragma unroll
-              for (int ni = 0; ni < NI; ++ni)
-                p.vt[seg * p.kv_seg_stride + chead[ni] * p.kv_head_stride + (long)cjj[ni] * p.kv_cap + k1] =
-                    (__bf16)(acc[mi][ni][4 * q + e] * scale);
-              step(seg, tt);
+              v[e] = acc[mi][ni][4 * q + e] * scale;
+              if (KIND == GEMM_FFN_UP) v[e] = gelu_as(v[e]);
             }
-            continue;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (r0 + e >= M) break;
-            const int ti = tt * rm.row_mult + g;
-            __bf16* base;
-            if (typ == 0) {
-              const int qi = ti - p.q_from;
-              base = qi < 0 ? nullptr : p.q + seg * p.q_seg_stride + (long)qi * p.dh;
+            char* dst = stg + (mi * 32 + (lane & 31)) * SP + (ni * 32 + 8 * q + 4 * (lane >> 5)) * 2;
+            if (KIND == GEMM_FFN_UP) {
+              const f16x4 o = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+              *(f16x4*)dst = o;
             } else {
-              base = (typ == 1 ? p.k : p.v) + seg * p.kv_seg_stride + (p.kv_slot_base + ti) * (long)p.dh;
+              const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+              *(bf16x4*)dst = o;
             }
-            if (base != nullptr) {
+          }
+      const int row_w0 = m0 + wm * TM, col_w0 = n0 + wn * TN;
+      constexpr int CPR = TN / 8;  // 16-byte chunks per staged row
+      if (KIND == GEMM_FFN_UP) {
 #pragma unroll
-              for (int ni = 0; ni < NI; ++ni) base[cofs[ni]] = (__bf16)(acc[mi][ni][4 * q + e] * scale);
+        for (int i = 0; i < TM * CPR / 64; ++i) {
+          const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
+          const int row = row_w0 + r;
+          if (row >= M) continue;
+          const uint4 val = *(const uint4*)(stg + r * SP + ch * 16);
+          int seg, tt;
+          split_row(row, rps, inv_rps, seg, tt);
+          *(uint4*)(p.hid_out + hid_row(rm, seg, tt, g) * N + col_w0 + ch * 8) = val;
+        }
+      } else {
+        // BN divides d, so the whole tile lies in one of Q, K, V
+        const int typ = n0 / p.d;
+        const int dsh = p.dh == 64 ? 6 : 5;
+        const int cin0 = col_w0 - typ * p.d;  // first column of this wave inside the d-wide block
+        if (typ == 2 && p.vt != nullptr) {
+          // transposed V: a lane takes one column and eight consecutive rows (key slots)
+#pragma unroll 1
+          for (int idx = lane; idx < TN * (TM / 8); idx += 64) {
+            const int c = idx % TN, r8 = (idx / TN) * 8;
+            const int row0 = row_w0 + r8;
+            if (row0 >= M) continue;
+            const int cc = cin0 + c, head = cc >> dsh, jj = cc & (p.dh - 1);
+            __bf16 vals[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vals[e] = *(const __bf16*)(stg + (r8 + e) * SP + c * 2);
+            int seg, tt;
+            split_row(row0, rps, inv_rps, seg, tt);
+            __bf16* colp = p.vt + seg * p.kv_seg_stride + head * p.kv_head_stride + (long)jj * p.kv_cap;
+            const long ki = p.kv_slot_base + (long)tt * rmult + g;
+            if (rmult == 1 && row0 + 7 < M && tt + 7 < rps && (ki & 7) == 0) {
+              *(uint4*)(colp + ki) = *(const uint4*)vals;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                if (row0 + e >= M) break;
+                colp[p.kv_slot_base + (long)tt * rmult + g] = vals[e];
+                if (++tt >= rps) {
+                  tt = 0;
+                  ++seg;
+                  colp = p.vt + seg * p.kv_seg_stride + head * p.kv_head_stride + (long)jj * p.kv_cap;
+                }
+              }
             }
-            step(seg, tt);
+          }
+        } else {
+          __bf16* const out = typ == 0 ? p.q : (typ == 1 ? p.k : p.v);
+          const long head_stride = typ == 0 ? p.q_head_stride : p.kv_head_stride;
+#pragma unroll
+          for (int i = 0; i < TM * CPR / 64; ++i) {
+            const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
+            const int row = row_w0 + r;
+            if (row >= M) continue;
+            const uint4 val = *(const uint4*)(stg + r * SP + ch * 16);
+            int seg, tt;
+            split_row(row, rps, inv_rps, seg, tt);
+            const long ti = (long)tt * rmult + g;
+            const int cc = cin0 + ch * 8, head = cc >> dsh, jj = cc & (p.dh - 1);
+            long o;
+            if (typ == 0) {
+              if (ti < p.q_from) continue;
+              o = seg * p.q_seg_stride + (ti - p.q_from) * p.dh;
+            } else {
+              o = seg * p.kv_seg_stride + (p.kv_slot_base + ti) * p.dh;
+            }
+            *(uint4*)(out + o + head * head_stride + jj) = val;
           }
         }
+      }
     }
   }
+}
+
+// Tile shapes: (BM, BN, compute waves along M). The operand ring takes what the output
+// staging leaves of the 160 KB of LDS, up to 8 stages.
+template <int KD, int BM, int BN, int WM, bool FP8>
+constexpr int stages_for() {
+  constexpr int stage = BM * 128 + BN * (FP8 ? 64 : 128);
+  constexpr int stg = KD == GEMM_FFN_DOWN ? 0 : 4 * (BM / WM) * ((BN / (4 / WM)) * 2 + 16);
+  constexpr int n = (159 * 1024 - stg) / stage;
+  return n > 8 ? 8 : n;
+}
+
+template <int KD, bool FP8, int SIDE, int BM, int BN, int WM>
+void launch_one(const GemmParams& p, hipStream_t s) {
+  const int tm = (p.M + BM - 1) / BM, tn = p.N / BN;
+  const long items = (long)tm * tn * p.groups;
+  const int grid = (int)(items < 256 ? items : 256);  // one workgroup per CU
+  hipLaunchKernelGGL((gemm_kernel<KD, FP8, SIDE, BM, BN, stages_for<KD, BM, BN, WM, FP8>(), WM>), dim3(grid), dim3(512), 0, s,
+                     p, tm, tn, (int)items);
+}
+
+template <int KD, int SIDE, int BM, int BN, int WM>
+void launch_cfg(bool fp8, const GemmParams& p, hipStream_t s) {
+  if constexpr (SIDE == 1 && BN != 96) {
+    if (fp8) {
+      launch_one<KD, true, SIDE, BM, BN, WM>(p, s);
+      return;
+    }
+  }
+  launch_one<KD, false, SIDE, BM, BN, WM>(p, s);
 }
 
 struct TileCfg {
   int bm, bn;
 };
 
-template <int KD, bool FP8, int SIDE, int BM, int BN, int BK, int ST, int WPC>
-void launch_one(const GemmParams& p, hipStream_t s) {
-  const int tm = (p.M + BM - 1) / BM, tn = p.N / BN;
-  const long items = (long)tm * tn * p.groups;
-  const int grid = (int)(items < WPC * 256 ? items : WPC * 256);
-  hipLaunchKernelGGL((gemm_kernel<KD, FP8, SIDE, BM, BN, BK, ST, WPC>), dim3(grid), dim3(256), 0, s, p, tm, tn,
-                     (int)items);
-}
-
-template <int KD, int SIDE, int BM, int BN>
-void launch_cfg(bool fp8, const GemmParams& p, hipStream_t s) {
-  if constexpr (SIDE == 1) {
-    if (fp8) {
-      launch_one<KD, true, SIDE, BM, BN, 64, 3, 2>(p, s);
-      return;
-    }
-  }
-  if constexpr (BM * BN >= 128 * 128) launch_one<KD, false, SIDE, BM, BN, 32, 4, 2>(p, s);
-  else launch_one<KD, false, SIDE, BM, BN, 64, 3, 2>(p, s);
-}
-
-// Cost model for the tile choice: the busiest CU's share of output tiles times the
-// tile's work, with a penalty for small tiles, whose operand traffic per flop is higher.
-double tile_cost(const GemmParams& p, int bm, int bn) {
+// The GEMMs here are bound by the L2 -> LDS operand feed, so the cost of a tile shape is
+// the busiest CU's item count times the operand bytes per item and k.
+double tile_cost(const GemmParams& p, bool fp8, int bm, int bn) {
   const long items = (long)((p.M + bm - 1) / bm) * (p.N / bn) * p.groups;
-  const double per_cu = (double)((items + 255) / 256);
-  const double work = (double)bm * bn;
-  const double pen = bm * bn >= 128 * 128 ? 1.0 : (bm * bn >= 128 * 64 ? 1.2 : 1.6);
-  return per_cu * work * pen;
+  return (double)((items + 255) / 256) * (bm + bn * (fp8 ? 0.5 : 1.0));
 }
 
 template <int KD, int SIDE>
 void launch_kind(bool fp8, const GemmParams& p, hipStream_t s) {
-  // BN = 128 needs N % 128 == 0 and, for Q / K / V, d % 128 == 0 (a tile never straddles two of them)
-  const bool n128 = p.N % 128 == 0 && (KD != GEMM_QKV || p.d % 128 == 0);
-  const TileCfg cands[3] = {{128, 128}, {128, 64}, {64, 64}};
+  // a Q / K / V tile must not straddle two of them: BN divides d
+  auto fits = [&](int bn) { return p.N % bn == 0 && (KD != GEMM_QKV || p.d % bn == 0) && !(fp8 && bn == 96); };
+  const TileCfg cands[4] = {{128, 128}, {128, 96}, {128, 64}, {64, 64}};
   int best = -1;
   double best_cost = 0;
-  for (int i = 0; i < 3; ++i) {
-    if (cands[i].bn == 128 && !n128) continue;
-    const double c = tile_cost(p, cands[i].bm, cands[i].bn);
+  for (int i = 0; i < 4; ++i) {
+    if (!fits(cands[i].bn)) continue;
+    const double c = tile_cost(p, fp8, cands[i].bm, cands[i].bn);
     if (best < 0 || c < best_cost) { best = i; best_cost = c; }
   }
-  if (best == 0) launch_cfg<KD, SIDE, 128, 128>(fp8, p, s);
-  else if (best == 1) launch_cfg<KD, SIDE, 128, 64>(fp8, p, s);
-  else launch_cfg<KD, SIDE, 64, 64>(fp8, p, s);
+  switch (best) {
+    case 0: launch_cfg<KD, SIDE, 128, 128, 2>(fp8, p, s); break;
+    case 1: launch_cfg<KD, SIDE, 128, 96, 4>(fp8, p, s); break;
+    case 2: launch_cfg<KD, SIDE, 128, 64, 2>(fp8, p, s); break;
+    default: launch_cfg<KD, SIDE, 64, 64, 2>(fp8, p, s); break;
+  }
 }
 
 }  // namespace
