@@ -89,6 +89,56 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&s
   st.l += ps;
 }
 
+// One 64-key tile against a wave's 32 queries: S^T = K Q^T, masking when a bound falls
+// inside the tile, the online-softmax update and O^T += V^T P^T. sb holds the tile: K rows
+// (XOR-swizzled 16-byte chunks) followed by V^T rows of 64 keys (128 bytes each).
+template <int DH>
+__device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, int my_lim, bool edge,
+                                          const bf16x8 (&qf)[DH / 16], Softmax<DH>& st, float scale) {
+  constexpr int KROW = DH * 2, K_BYTES = KT * KROW, KCH = KROW / 16;
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  f32x16 sc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sc[kb][j] = 0.f;
+    const int r = kb * 32 + l32;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+      const int c = 2 * s + half;
+      const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+      const bf16x8 a = *(const bf16x8*)(sb + r * KROW + cs * 16);
+      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[kb], 0, 0, 0);
+    }
+  }
+  if (edge) {  // a mask boundary falls inside this tile
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int slot = t0 + kb * 32 + 8 * (j >> 2) + half * 4 + (j & 3);
+        if (slot < key_lo || slot >= my_lim) sc[kb][j] = -INFINITY;
+      }
+  }
+  bf16x8 pb[2][2];
+  softmax_update<DH, 2>(st, sc, pb, scale);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) {
+        // keys kb*32 + 16c + 4*half + {0..3} and + 8: chunk 4kb + 2c (+1), byte 8*half
+        const int r = db * 32 + l32;
+        const int ch = 4 * kb + 2 * c;
+        const char* row = sb + K_BYTES + r * 128 + half * 8;
+        const bf16x4 lo = *(const bf16x4*)(row + ((ch ^ ((r >> 1) & 7)) << 4));
+        const bf16x4 hi = *(const bf16x4*)(row + (((ch + 1) ^ ((r >> 1) & 7)) << 4));
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][c], st.o[db], 0, 0, 0);
+      }
+}
+
 template <int DH, bool NS, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   constexpr int KROW = DH * 2;                // bytes per K row (64 or 128)
@@ -189,47 +239,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
     if (it + STAGES - 1 < ntiles) issue(t_first + (it + STAGES - 1) * KT, (it + STAGES - 1) % STAGES);
     const int t0 = t_first + it * KT;
     if (wave_live && t0 < wave_lim) {
-      const char* sb = smem + (it % STAGES) * STAGE;
-      f32x16 sc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sc[kb][j] = 0.f;
-        const int r = kb * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < DH / 16; ++s) {
-          const int c = 2 * s + half;
-          const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
-          const bf16x8 a = *(const bf16x8*)(sb + r * KROW + cs * 16);
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[kb], 0, 0, 0);
-        }
-      }
-      if (t0 < key_lo || t0 + KT > wave_lim_lo) {  // a mask boundary falls inside this tile
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int slot = t0 + kb * 32 + 8 * (j >> 2) + half * 4 + (j & 3);
-            if (slot < key_lo || slot >= my_lim) sc[kb][j] = -INFINITY;
-          }
-      }
-      bf16x8 pb[2][2];
-      softmax_update<DH, 2>(st, sc, pb, p.scale_log2);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int db = 0; db < DH / 32; ++db) {
-            // keys kb*32 + 16c + 4*half + {0..3} and + 8: chunk 4kb + 2c (+1), byte 8*half
-            const int r = db * 32 + l32;
-            const int ch = 4 * kb + 2 * c;
-            const char* row = sb + K_BYTES + r * 128 + half * 8;
-            const bf16x4 lo = *(const bf16x4*)(row + ((ch ^ ((r >> 1) & 7)) << 4));
-            const bf16x4 hi = *(const bf16x4*)(row + (((ch + 1) ^ ((r >> 1) & 7)) << 4));
-            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][c], st.o[db], 0, 0, 0);
-          }
+      attn_tile<DH>(smem + (it % STAGES) * STAGE, t0, key_lo, my_lim, t0 < key_lo || t0 + KT > wave_lim_lo, qf, st,
+                    p.scale_log2);
     }
   }
 
@@ -295,6 +306,141 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   }
 }
 
+// S-token attention with the keys of one 32-query block split over KS waves: wave w takes
+// key tiles w, w + KS, ... through a private 2-stage LDS ring (no barriers while
+// streaming), and the partial (max, sum, O) of the waves merge through LDS at the end.
+// Used when there are few query blocks and long key ranges (one user's prefill, appends),
+// where the plain kernel's critical path is one wave walking every key tile.
+template <int DH, int KS>
+__global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
+  constexpr int KROW = DH * 2;
+  constexpr int K_BYTES = KT * KROW;
+  constexpr int V_BYTES = DH * KT * 2;
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int K_INSTR = K_BYTES / 1024, V_INSTR = V_BYTES / 1024;  // per tile, one wave
+  constexpr int PER_TILE = K_INSTR + V_INSTR;
+  constexpr int KCH = KROW / 16, KRPI = 64 / KCH;
+  constexpr int MERGE = 64 * (2 + 16 * (DH / 32)) * 4;  // per wave: m, l and O of 64 lanes
+  constexpr int SMEM = KS * 2 * STAGE > KS * MERGE ? KS * 2 * STAGE : KS * MERGE;
+  static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "tile split");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int h = blockIdx.y, seg = blockIdx.z;
+  const int wq0 = blockIdx.x * 32;
+  const int qi = wq0 + l32;
+  const bool q_ok = qi < p.nq;
+
+  bf16x8 qf[DH / 16];
+  {
+    const __bf16* qrow = p.q + seg * p.q_seg_stride + h * p.q_head_stride + (long)(q_ok ? qi : 0) * DH;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+      bf16x8 v = *(const bf16x8*)(qrow + s * 16 + half * 8);
+      if (!q_ok) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.f;
+      }
+      qf[s] = v;
+    }
+  }
+  const int vf = p.valid_from[seg];
+  const int key_lo = max(0, vf - p.key_pos0);
+  const int qlast = min(wq0 + 31, p.nq - 1);
+  const int key_hi = min(p.n_keys, p.q_pos0 + qlast - p.key_pos0 + 1);  // exclusive, this block
+  const int lim_lo = wq0 + 31 < p.nq ? min(p.n_keys, p.q_pos0 + wq0 - p.key_pos0 + 1) : 0;
+  const int my_lim = q_ok ? min(p.n_keys, p.q_pos0 + qi - p.key_pos0 + 1) : 0;
+
+  Softmax<DH> st;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st.o[db][j] = 0.f;
+
+  const int t_first = (key_lo / KT) * KT;
+  const int ntiles = key_hi > t_first ? (key_hi - t_first + KT - 1) / KT : 0;
+  const int n_my = wave < ntiles ? (ntiles - wave + KS - 1) / KS : 0;
+  const char* kbase = (const char*)(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride);
+  const char* vbase = (const char*)(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride);
+  char* ring = smem + wave * 2 * STAGE;
+  auto issue = [&](int j) {
+    const int t0 = t_first + (wave + j * KS) * KT;
+    char* sb = ring + (j & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < K_INSTR; ++i) {
+      const int r = i * KRPI + lane / KCH, c = lane % KCH;
+      const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+      dma16(kbase + (long)(t0 + r) * KROW + cs * 16, (lds_void*)(sb + i * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < V_INSTR; ++i) {
+      const int r = i * 8 + (lane >> 3);  // dh row
+      dma16(vbase + ((long)r * p.kv_cap + t0) * 2 + ((((lane & 7) ^ ((r >> 1) & 7))) << 4),
+            (lds_void*)(sb + K_BYTES + i * 1024));
+    }
+  };
+  if (n_my > 0) issue(0);
+#pragma unroll 1
+  for (int j = 0; j < n_my; ++j) {
+    if (j + 1 < n_my) {
+      issue(j + 1);
+      wait_vmcnt<PER_TILE>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    const int t0 = t_first + (wave + j * KS) * KT;
+    attn_tile<DH>(ring + (j & 1) * STAGE, t0, key_lo, my_lim, t0 < key_lo || t0 + KT > lim_lo, qf, st,
+                  p.scale_log2);
+  }
+
+  // ---- merge: every wave's lane l holds the same query and O layout ----
+  __syncthreads();  // all rings are done; reuse the LDS for the partial results
+  float* mw = (float*)(smem + wave * MERGE);
+  mw[lane] = st.m;
+  mw[64 + lane] = st.l + __shfl_xor(st.l, 32);
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mw[128 + (db * 16 + j) * 64 + lane] = st.o[db][j];
+  __syncthreads();
+  if (wave != 0 || !q_ok) return;
+  float m_all = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < KS; ++w) m_all = fmaxf(m_all, ((const float*)(smem + w * MERGE))[lane]);
+  float l_all = 0.f;
+  f32x16 o[DH / 32];
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
+#pragma unroll
+  for (int w = 0; w < KS; ++w) {
+    const float* src = (const float*)(smem + w * MERGE);
+    const float mwv = src[lane];
+    const float f = mwv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mwv - m_all) * p.scale_log2);
+    l_all += src[64 + lane] * f;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[db][j] += src[128 + (db * 16 + j) * 64 + lane] * f;
+  }
+  const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
+  float* rrow = p.res + seg * p.res_seg_stride + (p.res_row_base + qi) * p.res_row_stride + h * DH;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      float4* dst = (float4*)(rrow + db * 32 + 8 * gi + half * 4);
+      float4 r = *dst;
+      r.x += o[db][4 * gi + 0] * inv;
+      r.y += o[db][4 * gi + 1] * inv;
+      r.z += o[db][4 * gi + 2] * inv;
+      r.w += o[db][4 * gi + 3] * inv;
+      *dst = r;
+    }
+}
+
 // Zero the K rows and V^T columns [from, cap) of every (user, head) block, so
 // that key tiles reaching past the filled length read finite values.
 __global__ void cache_clear_tail_kernel(__bf16* k, __bf16* vt, int blocks, int dh, int cap, int from) {
@@ -327,7 +473,22 @@ void launch_attn_nw(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t
 hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s) {
   if (p.nq <= 0 || n_seg <= 0) return hipSuccess;
   if (p.kv_cap % KT != 0 || (dh != 32 && dh != 64)) return hipErrorInvalidValue;
-  launch_attn_nw<4>(ns, dh, p, n_seg, s);
+  // 32 queries per wave; a workgroup's waves share the K/V tiles. Fewer waves per workgroup
+  // when the grid would leave CUs idle (one user's prefill has few query blocks per head);
+  // the K/V of a layer is L2-resident, so streaming it to more workgroups is cheap.
+  const long blocks32 = (long)((p.nq + 31) / 32) * p.H * n_seg;
+  if (!ns && blocks32 < 2L * 512) {
+    // few S query blocks: split each block's keys over four waves
+    dim3 grid((p.nq + 31) / 32, p.H, n_seg);
+    if (dh == 64) hipLaunchKernelGGL((attn_split_kernel<64, 4>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((attn_split_kernel<32, 4>), grid, dim3(256), 0, s, p);
+  } else if (blocks32 >= 4L * 512) {
+    launch_attn_nw<4>(ns, dh, p, n_seg, s);
+  } else if (blocks32 >= 2L * 512) {
+    launch_attn_nw<2>(ns, dh, p, n_seg, s);
+  } else {
+    launch_attn_nw<1>(ns, dh, p, n_seg, s);
+  }
   return hipGetLastError();
 }
 
