@@ -206,8 +206,8 @@ int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* 
 typedef enum {
   ONETRANS_K_S_QKV = 0, ONETRANS_K_S_ATTN = 1, ONETRANS_K_S_FFN_UP = 2, ONETRANS_K_S_FFN_DOWN = 3,
   ONETRANS_K_NS_QKV = 4, ONETRANS_K_NS_ATTN = 5, ONETRANS_K_NS_FFN_UP = 6, ONETRANS_K_NS_FFN_DOWN = 7,
-  ONETRANS_K_ELEMENTWISE = 8, ONETRANS_K_S_NORM = 9, ONETRANS_K_NS_NORM = 10, ONETRANS_K_NS_FFN = 11,
-  ONETRANS_K_COUNT = 12
+  ONETRANS_K_ELEMENTWISE = 8, ONETRANS_K_S_NORM = 9, ONETRANS_K_NS_NORM = 10,
+  ONETRANS_K_COUNT = 11
 } onetrans_kernel_family;
 int onetrans_kernel_timing_enable(uint32_t mask);
 int onetrans_kernel_timing_read(int family, double* total_ms, int64_t* launches);

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libonetrans.so")
-SOURCES = ["gemm.hip", "attention.hip", "ffn.hip", "elementwise.hip", "onetrans_api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "onetrans_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -60,38 +60,17 @@ __device__ __forceinline__ void split_row(int row, int rps, float inv_rps, int& 
   else if (t >= rps) { ++seg; t -= rps; }
 }
 
-// Exact OCP E4M3FN -> fp16 for the two codes held in bits 0-7 and 16-23 of x.
-// Normal codes: the fp16 exponent is the E4M3 exponent field + 8 (bias 15 vs 7),
-// mantissa bits move up by 7. Zero / subnormal codes (exponent field 0) are
-// m * 2^-9, taken through an exact float conversion.
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t x) {
-  uint32_t r = (((x & 0x007F007Fu) << 7) + 0x20002000u) | ((x & 0x00800080u) << 8);
-  if (__builtin_expect(((x & 0x00000078u) == 0) || ((x & 0x00780000u) == 0), 0)) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      uint32_t c = (x >> (16 * hh)) & 0xFFu;
-      if ((c & 0x78u) == 0) {
-        _Float16 v = (_Float16)((float)(c & 7u) * 0.001953125f);
-        uint32_t bits = (uint32_t)__builtin_bit_cast(uint16_t, v) | ((c & 0x80u) << 8);
-        r = (r & ~(0xFFFFu << (16 * hh))) | (bits << (16 * hh));
-      }
-    }
-  }
-  return r;
-}
-
-// 8 E4M3 codes (two dwords) -> 8 halfs in order.
+// 8 OCP E4M3FN codes (two dwords, code i in byte i) -> 8 halfs in order, with the gfx950
+// conversion instruction at scale 1, which is exact: every E4M3FN value, subnormals
+// included, is an fp16 value.
 __device__ __forceinline__ f16x8 e4m3x8_to_f16(uint2 c) {
-  const uint32_t in[2] = {c.x, c.y};
-  uint32_t out[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t a = e4m3x2_to_f16x2(in[i] & 0x00FF00FFu);         // codes 0, 2
-    const uint32_t b = e4m3x2_to_f16x2((in[i] >> 8) & 0x00FF00FFu);  // codes 1, 3
-    out[2 * i] = (a & 0xFFFFu) | (b << 16);
-    out[2 * i + 1] = (a >> 16) | (b & 0xFFFF0000u);
-  }
-  return __builtin_bit_cast(f16x8, make_uint4(out[0], out[1], out[2], out[3]));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.0f, true);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.0f, false);
+  const f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.0f, true);
+  const f16x8 r = {a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+  return r;
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
@@ -147,14 +126,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
   constexpr int A_CPR = AROW / 16, B_CPR = BROW / 16;      // 16-byte chunks per row
   static_assert(WM * WN == 4 && TM % 32 == 0 && TN % 32 == 0, "wave grid");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "tile shape");
-  // wave-private output staging (16-bit outputs): TM rows of TN values, rows padded by 16 bytes
-  constexpr bool STAGED = KIND != GEMM_FFN_DOWN;
-  constexpr int SP = TN * 2 + 16;                       // staging row pitch in bytes
-  constexpr int WSTG = STAGED ? TM * SP : 0;            // per compute wave
-  static_assert(STAGES >= 2 && STAGES * STAGE + 4 * WSTG <= 159 * 1024, "LDS");
+  constexpr bool STAGED = KIND != GEMM_FFN_DOWN;  // 16-bit outputs written from registers
+  static_assert(STAGES >= 2 && STAGES * STAGE <= 159 * 1024, "LDS");
   static_assert(PT * (STAGES - 2) < 64, "vmcnt range");
-  static_assert(TM * (TN / 8) % 64 == 0, "staged chunks per lane");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE + 4 * WSTG];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const RowMap rm = p.rm;
@@ -328,115 +303,95 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
         }
       }
     } else {
-      // ---- staged epilogue (Q / K / V and the GELU hidden rows). With the weight fragment
-      // first, lane holds output row (lane % 32) of each 32x32 block and, in registers
-      // 4q..4q+3, columns 8q + 4*(lane/32) + 0..3. They go to this wave's LDS staging rows
-      // (8 bytes per write), come back as 16-byte row chunks and leave as 16-byte stores. ----
-      char* stg = smem + STAGES * STAGE + wave * WSTG;
+      // ---- 16-bit outputs (Q / K / V, GELU hidden rows), straight from registers. With the
+      // weight fragment first, lane holds output row (lane % 32) of each 32x32 block and, in
+      // registers 4q..4q+3, columns 8q + 4*(lane/32) + 0..3. Packed to 16-bit pairs, groups
+      // q and q+1 trade halves across the two half-waves (v_permlane32_swap), after which a
+      // lane holds 8 consecutive columns of one group: one 16-byte store each. ----
+      const int half = lane >> 5;
+      const int col_l = n0 + wn * TN;          // + ni*32 + 8*(qq + half)
+      const int row_l = m0 + wm * TM + (lane & 31);  // + mi*32
+      auto pack2 = [&](float x, float y) -> uint32_t {
+        if (KIND == GEMM_FFN_UP) {
+          const _Float16 hx = (_Float16)x, hy = (_Float16)y;
+          return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+        }
+        const __bf16 bx = (__bf16)x, by = (__bf16)y;
+        return (uint32_t)__builtin_bit_cast(uint16_t, bx) | ((uint32_t)__builtin_bit_cast(uint16_t, by) << 16);
+      };
+      auto val = [&](float x) { return KIND == GEMM_FFN_UP ? gelu_as(x * scale) : x * scale; };
+      const int typ = KIND == GEMM_QKV ? n0 / p.d : 0;
+      const bool vt_mode = KIND == GEMM_QKV && typ == 2 && p.vt != nullptr;
+      const int dsh = p.dh == 64 ? 6 : 5;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = row_l + mi * 32;
+        if (row >= M) continue;
+        int seg, tt;
+        split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
+        if (vt_mode) {
+          // transposed V: lanes hold 32 consecutive key slots of each column
+          __bf16* base = p.vt + seg * p.kv_seg_stride + p.kv_slot_base + (long)tt * rm.row_mult + g;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int cc = col_l - typ * p.d + ni * 32 + 8 * q + 4 * half + e;
+                base[(cc >> dsh) * p.kv_head_stride + (long)(cc & (p.dh - 1)) * p.kv_cap] =
+                    (__bf16)(acc[mi][ni][4 * q + e] * scale);
+              }
+          continue;
+        }
+        long rbase;  // element offset of this row's first column (16-bit outputs)
+        long head_stride = 0;
+        __bf16* out = nullptr;
+        if (KIND == GEMM_FFN_UP) {
+          rbase = hid_row(rm, seg, tt, g) * N;
+        } else {
+          const long ti = (long)tt * rm.row_mult + g;
+          if (typ == 0) {
+            if (ti < p.q_from) continue;
+            rbase = seg * p.q_seg_stride + (ti - p.q_from) * p.dh;
+            head_stride = p.q_head_stride;
+            out = p.q;
+          } else {
+            rbase = seg * p.kv_seg_stride + (p.kv_slot_base + ti) * p.dh;
+            head_stride = p.kv_head_stride;
+            out = typ == 1 ? p.k : p.v;
+          }
+        }
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v[e] = acc[mi][ni][4 * q + e] * scale;
-              if (KIND == GEMM_FFN_UP) v[e] = gelu_as(v[e]);
-            }
-            char* dst = stg + (mi * 32 + (lane & 31)) * SP + (ni * 32 + 8 * q + 4 * (lane >> 5)) * 2;
+          for (int qq = 0; qq < 4; qq += 2) {
+            const f32x16& v = acc[mi][ni];
+            const int j0 = 4 * qq, j1 = 4 * qq + 4;
+            const auto lo = __builtin_amdgcn_permlane32_swap(pack2(val(v[j0]), val(v[j0 + 1])),
+                                                             pack2(val(v[j1]), val(v[j1 + 1])), false, false);
+            const auto hi = __builtin_amdgcn_permlane32_swap(pack2(val(v[j0 + 2]), val(v[j0 + 3])),
+                                                             pack2(val(v[j1 + 2]), val(v[j1 + 3])), false, false);
+            const uint4 chunk = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+            const int c = col_l + ni * 32 + 8 * (qq + half);
             if (KIND == GEMM_FFN_UP) {
-              const f16x4 o = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-              *(f16x4*)dst = o;
+              *(uint4*)(p.hid_out + rbase + c) = chunk;
             } else {
-              const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-              *(bf16x4*)dst = o;
+              const int cc = c - typ * p.d;
+              *(uint4*)(out + rbase + (cc >> dsh) * head_stride + (cc & (p.dh - 1))) = chunk;
             }
           }
-      const int row_w0 = m0 + wm * TM, col_w0 = n0 + wn * TN;
-      constexpr int CPR = TN / 8;  // 16-byte chunks per staged row
-      if (KIND == GEMM_FFN_UP) {
-#pragma unroll
-        for (int i = 0; i < TM * CPR / 64; ++i) {
-          const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
-          const int row = row_w0 + r;
-          if (row >= M) continue;
-          const uint4 val = *(const uint4*)(stg + r * SP + ch * 16);
-          int seg, tt;
-          split_row(row, rps, inv_rps, seg, tt);
-          *(uint4*)(p.hid_out + hid_row(rm, seg, tt, g) * N + col_w0 + ch * 8) = val;
-        }
-      } else {
-        // BN divides d, so the whole tile lies in one of Q, K, V
-        const int typ = n0 / p.d;
-        const int dsh = p.dh == 64 ? 6 : 5;
-        const int cin0 = col_w0 - typ * p.d;  // first column of this wave inside the d-wide block
-        if (typ == 2 && p.vt != nullptr) {
-          // transposed V: a lane takes one column and eight consecutive rows (key slots)
-#pragma unroll 1
-          for (int idx = lane; idx < TN * (TM / 8); idx += 64) {
-            const int c = idx % TN, r8 = (idx / TN) * 8;
-            const int row0 = row_w0 + r8;
-            if (row0 >= M) continue;
-            const int cc = cin0 + c, head = cc >> dsh, jj = cc & (p.dh - 1);
-            __bf16 vals[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vals[e] = *(const __bf16*)(stg + (r8 + e) * SP + c * 2);
-            int seg, tt;
-            split_row(row0, rps, inv_rps, seg, tt);
-            __bf16* colp = p.vt + seg * p.kv_seg_stride + head * p.kv_head_stride + (long)jj * p.kv_cap;
-            const long ki = p.kv_slot_base + (long)tt * rmult + g;
-            if (rmult == 1 && row0 + 7 < M && tt + 7 < rps && (ki & 7) == 0) {
-              *(uint4*)(colp + ki) = *(const uint4*)vals;
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                if (row0 + e >= M) break;
-                colp[p.kv_slot_base + (long)tt * rmult + g] = vals[e];
-                if (++tt >= rps) {
-                  tt = 0;
-                  ++seg;
-                  colp = p.vt + seg * p.kv_seg_stride + head * p.kv_head_stride + (long)jj * p.kv_cap;
-                }
-              }
-            }
-          }
-        } else {
-          __bf16* const out = typ == 0 ? p.q : (typ == 1 ? p.k : p.v);
-          const long head_stride = typ == 0 ? p.q_head_stride : p.kv_head_stride;
-#pragma unroll
-          for (int i = 0; i < TM * CPR / 64; ++i) {
-            const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
-            const int row = row_w0 + r;
-            if (row >= M) continue;
-            const uint4 val = *(const uint4*)(stg + r * SP + ch * 16);
-            int seg, tt;
-            split_row(row, rps, inv_rps, seg, tt);
-            const long ti = (long)tt * rmult + g;
-            const int cc = cin0 + ch * 8, head = cc >> dsh, jj = cc & (p.dh - 1);
-            long o;
-            if (typ == 0) {
-              if (ti < p.q_from) continue;
-              o = seg * p.q_seg_stride + (ti - p.q_from) * p.dh;
-            } else {
-              o = seg * p.kv_seg_stride + (p.kv_slot_base + ti) * p.dh;
-            }
-            *(uint4*)(out + o + head * head_stride + jj) = val;
-          }
-        }
       }
     }
   }
 }
 
-// Tile shapes: (BM, BN, compute waves along M). The operand ring takes what the output
-// staging leaves of the 160 KB of LDS, up to 8 stages.
+// Tile shapes: (BM, BN, compute waves along M). The operand ring takes up to 159 KB of
+// LDS, at most 8 stages.
 template <int KD, int BM, int BN, int WM, bool FP8>
 constexpr int stages_for() {
   constexpr int stage = BM * 128 + BN * (FP8 ? 64 : 128);
-  constexpr int stg = KD == GEMM_FFN_DOWN ? 0 : 4 * (BM / WM) * ((BN / (4 / WM)) * 2 + 16);
-  constexpr int n = (159 * 1024 - stg) / stage;
+  constexpr int n = (159 * 1024) / stage;
   return n > 8 ? 8 : n;
 }
 
@@ -475,18 +430,20 @@ template <int KD, int SIDE>
 void launch_kind(bool fp8, const GemmParams& p, hipStream_t s) {
   // a Q / K / V tile must not straddle two of them: BN divides d
   auto fits = [&](int bn) { return p.N % bn == 0 && (KD != GEMM_QKV || p.d % bn == 0) && !(fp8 && bn == 96); };
-  const TileCfg cands[4] = {{128, 128}, {128, 96}, {128, 64}, {64, 64}};
+  // ties go to the earlier entry: the smaller tile, which leaves fewer CUs idle in the last round
+  const TileCfg cands[5] = {{128, 96}, {128, 128}, {256, 128}, {128, 64}, {64, 64}};
   int best = -1;
   double best_cost = 0;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 5; ++i) {
     if (!fits(cands[i].bn)) continue;
     const double c = tile_cost(p, fp8, cands[i].bm, cands[i].bn);
     if (best < 0 || c < best_cost) { best = i; best_cost = c; }
   }
   switch (best) {
-    case 0: launch_cfg<KD, SIDE, 128, 128, 2>(fp8, p, s); break;
-    case 1: launch_cfg<KD, SIDE, 128, 96, 4>(fp8, p, s); break;
-    case 2: launch_cfg<KD, SIDE, 128, 64, 2>(fp8, p, s); break;
+    case 0: launch_cfg<KD, SIDE, 128, 96, 4>(fp8, p, s); break;
+    case 1: launch_cfg<KD, SIDE, 128, 128, 2>(fp8, p, s); break;
+    case 2: launch_cfg<KD, SIDE, 256, 128, 2>(fp8, p, s); break;
+    case 3: launch_cfg<KD, SIDE, 128, 64, 2>(fp8, p, s); break;
     default: launch_cfg<KD, SIDE, 64, 64, 2>(fp8, p, s); break;
   }
 }

@@ -8,44 +8,6 @@ namespace onetrans {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Reads of LDS tiles that arrive by DMA. Written as inline asm because the
-// compiler cannot tell which DMA a plain LDS load depends on and would wait for
-// every DMA still in flight (draining the pipeline) before each read. Each asm
-// block issues its reads and waits for them (lgkmcnt(0)) before it ends, so no
-// output register is ever seen before its data has landed. Addresses are LDS
-// byte addresses.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-__device__ __forceinline__ void lds_read_b128x1(u32x4& o0, uint32_t a0) {
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(o0) : "v"(a0));
-}
-__device__ __forceinline__ void lds_read_b128x2(u32x4& o0, u32x4& o1, uint32_t a0, uint32_t a1) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(o0), "=&v"(o1) : "v"(a0), "v"(a1));
-}
-__device__ __forceinline__ void lds_read_b128x3(u32x4& o0, u32x4& o1, u32x4& o2, uint32_t a0, uint32_t a1,
-                                                uint32_t a2) {
-  asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(o0), "=&v"(o1), "=&v"(o2) : "v"(a0), "v"(a1), "v"(a2));
-}
-__device__ __forceinline__ void lds_read_b128x4(u32x4& o0, u32x4& o1, u32x4& o2, u32x4& o3, uint32_t a0,
-                                                uint32_t a1, uint32_t a2, uint32_t a3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3) : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
-}
-__device__ __forceinline__ void lds_read_b64x4(u32x2& o0, u32x2& o1, u32x2& o2, u32x2& o3, uint32_t a0,
-                                               uint32_t a1, uint32_t a2, uint32_t a3) {
-  asm volatile(
-      "ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3) : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
-}
-
 // GELU(x) = x/2 (1 + erf(x / sqrt 2)) with erf from Abramowitz & Stegun,
 // Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 for all
 // x): erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0.
@@ -76,7 +38,7 @@ __device__ __forceinline__ void dma16(const void* g, lds_void* l) {
 
 // Row addressing shared by the GEMM prologue/epilogue.
 //
-// A GEMM covers `groups` groups (blockIdx.z) of M rows each. Row r of group g
+// A GEMM covers `groups` groups of M rows each. Row r of group g
 // decodes to seg = r / rows_per_seg, t = r % rows_per_seg, and touches:
 //   residual row : res + seg*res_seg_stride + (res_row_base + t)*res_row_stride + g*res_group_stride
 //   hidden row   : hid + ((seg*rows_per_seg + t)*row_mult + g) * ld_hid
@@ -151,25 +113,6 @@ struct NormParams {
   _Float16* out;
 };
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
-
-// Fused pre-norm FFN of the NS rows (one group per NS position):
-//   y = z + W2 GELU(W1 RMSNorm(z; gain)) in place on the residual rows, and, when
-//   next_xn is not NULL, next_xn = fp16 RMSNorm(y; next_gain) in hidden addressing.
-struct FfnParams {
-  int M, groups, d, F;
-  RowMap rm;
-  float* res;
-  const float* gain;          // [groups][d], stride gain_group_stride (also for next_gain)
-  long gain_group_stride;
-  float eps;
-  const void* w1; const void* w2;   // [groups][F][d], [groups][d][F]; fp16 or E4M3 codes
-  long w1_group_stride, w2_group_stride;  // elements
-  const float* wscale;        // E4M3 only: [group*5 + 3] (W1), [group*5 + 4] (W2)
-  const float* next_gain;
-  _Float16* next_xn;
-};
-bool ffn_fused_supported(int d, int F);
-hipError_t launch_ffn_fused(bool fp8, const FfnParams& p, hipStream_t s);
 
 // Elementwise helpers.
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, long n, hipStream_t s);

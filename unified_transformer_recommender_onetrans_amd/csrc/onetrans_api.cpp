@@ -286,8 +286,6 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
   return ONETRANS_OK;
 }
 
-constexpr int kFusedNsFfnMinCandidates = 1 << 30;  // measured crossover not reached yet
-
 int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const char* cache_buf, const size_t* k_off,
                const size_t* v_off, int n_users, int n_appended, int user, const uint16_t* ns_tokens, int C,
                float* ns_out, char* ws, hipStream_t st) {
@@ -305,14 +303,10 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     OT_HIP(launch_bf16_to_f32(ns_tokens, ns_out, rows * d, st), "NS input conversion launch");
   }
   const RowMap rm{C, s.P, 0, 0, P * d, d};
-  // The fused NS FFN keeps the hidden rows on chip but streams each weight chunk once per
-  // 64 candidates; with the persistent GEMMs the unfused pair measures faster at C = 256
-  // (OneTrans-L shape), so the fused kernel is used only for large candidate counts.
-  const bool fused = ffn_fused_supported(s.d, s.F) && C >= kFusedNsFfnMinCandidates;
   for (int l = 0; l < s.L; ++l) {
     const long cap = s.cap[l];
     const int len = s.n[l] + n_appended;
-    if (l == 0 || !fused) {  // with the fused FFN, layer l-1 already wrote this layer's pre-norm
+    {
       int rc = run_norm(s, ONETRANS_K_NS_NORM, C, s.P, rm, ns_out, (const float*)(pk + lo[l].ns_ga), d, xn, st);
       if (rc) return rc;
     }
@@ -348,20 +342,6 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
       OT_HIP(launch_attention(true, s.dh, at, 1, st), "NS attention launch");
     }
 
-    if (fused) {
-      FfnParams fp;
-      memset(&fp, 0, sizeof(fp));
-      fp.M = C; fp.groups = s.P; fp.d = s.d; fp.F = s.F; fp.rm = rm;
-      fp.res = ns_out; fp.gain = (const float*)(pk + lo[l].ns_gf); fp.gain_group_stride = d; fp.eps = s.eps;
-      fp.w1 = pk + lo[l].ns_w1; fp.w2 = pk + lo[l].ns_w2;
-      fp.w1_group_stride = (long)s.F * d; fp.w2_group_stride = d * s.F;
-      fp.wscale = (const float*)(pk + lo[l].ns_scale);
-      fp.next_gain = l + 1 < s.L ? (const float*)(pk + lo[l + 1].ns_ga) : nullptr;
-      fp.next_xn = l + 1 < s.L ? xn : nullptr;
-      FamilyTimer t(ONETRANS_K_NS_FFN, st);
-      OT_HIP(launch_ffn_fused(s.fp8, fp, st), "NS fused FFN launch");
-      continue;
-    }
     int rc = run_norm(s, ONETRANS_K_NS_NORM, C, s.P, rm, ns_out, (const float*)(pk + lo[l].ns_gf), d, xn, st);
     if (rc) return rc;
     GemmParams u = base_gemm(s);
