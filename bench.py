@@ -183,7 +183,7 @@ def timed(fn, steps, warmup, sync):
 FAMILY_SOURCES = {
     "s_qkv": "gemm.hip", "s_ffn_up": "gemm.hip", "s_ffn_down": "gemm.hip", "ns_qkv": "gemm.hip",
     "ns_ffn_up": "gemm.hip", "ns_ffn_down": "gemm.hip", "s_attn": "attention.hip", "ns_attn": "attention.hip",
-    "s_norm": "elementwise.hip", "ns_norm": "elementwise.hip", "elementwise": "elementwise.hip",
+    "elementwise": "elementwise.hip",
 }
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "unified_transformer_recommender_onetrans_amd", "csrc")

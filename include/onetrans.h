@@ -34,7 +34,11 @@
  *   - Numerics: RMSNorm, softmax and the residual stream in fp32; the five
  *     linear maps take fp16 operands (bf16 weights converted exactly at pack
  *     time, E4M3FN weights decoded exactly) with fp32 accumulation; attention
- *     takes bf16 Q, K, V and probabilities with fp32 accumulation.
+ *     takes bf16 Q, K, V and probabilities with fp32 accumulation. A norm
+ *     feeding a linear map is applied as r * ((x * g) W): the operand is
+ *     x * g rounded to fp16 and the row factor r = 1/sqrt(mean(x^2) + eps)
+ *     (fp32) scales the accumulator, so every |x_j g_j| of the residual
+ *     stream must stay within fp16 range (65504).
  *   - Not thread-safe for concurrent calls that share a workspace or a cache;
  *     calls on distinct workspaces and caches are independent.
  *   - onetrans_last_error() returns a thread-local description of the last
@@ -206,8 +210,8 @@ int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* 
 typedef enum {
   ONETRANS_K_S_QKV = 0, ONETRANS_K_S_ATTN = 1, ONETRANS_K_S_FFN_UP = 2, ONETRANS_K_S_FFN_DOWN = 3,
   ONETRANS_K_NS_QKV = 4, ONETRANS_K_NS_ATTN = 5, ONETRANS_K_NS_FFN_UP = 6, ONETRANS_K_NS_FFN_DOWN = 7,
-  ONETRANS_K_ELEMENTWISE = 8, ONETRANS_K_S_NORM = 9, ONETRANS_K_NS_NORM = 10,
-  ONETRANS_K_COUNT = 11
+  ONETRANS_K_ELEMENTWISE = 8,
+  ONETRANS_K_COUNT = 9
 } onetrans_kernel_family;
 int onetrans_kernel_timing_enable(uint32_t mask);
 int onetrans_kernel_timing_read(int family, double* total_ms, int64_t* launches);

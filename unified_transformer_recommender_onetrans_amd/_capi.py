@@ -69,7 +69,7 @@ EXPORTS = {
 }
 
 KERNEL_FAMILIES = ["s_qkv", "s_attn", "s_ffn_up", "s_ffn_down", "ns_qkv", "ns_attn", "ns_ffn_up", "ns_ffn_down",
-                   "elementwise", "s_norm", "ns_norm"]
+                   "elementwise"]
 
 
 def kernel_timing_enable(families) -> None:

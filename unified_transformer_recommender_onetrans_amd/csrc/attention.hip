@@ -26,6 +26,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int KT = 64;      // keys per tile
@@ -139,6 +140,79 @@ __device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, in
       }
 }
 
+// Output of query row qi, in two parts. out_row_load fetches this lane's half of head h's
+// residual columns (4 consecutive columns per register group) and, with EARLY_G, the FFN
+// norm's gains for them; kernels call it before streaming any key tile, so the loads
+// overlap the whole key loop (and, being older than every tile load, keep the tile waits
+// exact). Without EARLY_G (32 fewer registers held through the loop, for kernels whose
+// occupancy they would cut) the gains load in out_row_store, before any store.
+// out_row_store adds the normalised attention output, writes the residual back, then the
+// norm's operand x * g and the head's partial sum of squares (deferred RMSNorm, slot h).
+// Both lanes of the row's pair take part.
+template <int DH>
+struct OutRow {
+  float4 x[DH / 32][4];
+  float4 g[DH / 32][4];
+};
+
+template <int DH, bool EARLY_G>
+__device__ __forceinline__ void load_gains(const AttnParams& p, int h, int qi, OutRow<DH>& r) {
+  const NormOut& no = p.nout;
+  if (!no.xg) return;
+  const int half = (threadIdx.x >> 5) & 1;
+  const float* grow = no.gain + (long)(qi % p.P) * no.gain_group_stride + h * DH + half * 4;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) r.g[db][gi] = *(const float4*)(grow + db * 32 + 8 * gi);
+}
+
+template <int DH, bool EARLY_G>
+__device__ __forceinline__ void out_row_load(const AttnParams& p, int seg, int h, int qi, OutRow<DH>& r) {
+  const int half = (threadIdx.x >> 5) & 1;
+  const float* rrow = p.res + seg * p.res_seg_stride + (p.res_row_base + qi) * p.res_row_stride + h * DH + half * 4;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) r.x[db][gi] = *(const float4*)(rrow + db * 32 + 8 * gi);
+  if (EARLY_G) load_gains<DH, true>(p, h, qi, r);
+}
+
+template <int DH, bool EARLY_G>
+__device__ __forceinline__ void out_row_store(const AttnParams& p, int seg, int h, int qi, OutRow<DH>& r,
+                                              const f32x16 (&o)[DH / 32], float inv) {
+  const int half = (threadIdx.x >> 5) & 1;
+  if (!EARLY_G) load_gains<DH, false>(p, h, qi, r);
+  float* rrow = p.res + seg * p.res_seg_stride + (p.res_row_base + qi) * p.res_row_stride + h * DH + half * 4;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      float4& v = r.x[db][gi];
+      v.x += o[db][4 * gi + 0] * inv;
+      v.y += o[db][4 * gi + 1] * inv;
+      v.z += o[db][4 * gi + 2] * inv;
+      v.w += o[db][4 * gi + 3] * inv;
+      *(float4*)(rrow + db * 32 + 8 * gi) = v;
+    }
+  const NormOut& no = p.nout;
+  if (!no.xg) return;
+  const long hr = (long)seg * p.nq + qi;
+  _Float16* xrow = no.xg + hr * p.d + h * DH + half * 4;
+  float part = 0.f;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const float4 v = r.x[db][gi], g4 = r.g[db][gi];
+      part += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      const f16x4 hv = {(_Float16)(v.x * g4.x), (_Float16)(v.y * g4.y), (_Float16)(v.z * g4.z), (_Float16)(v.w * g4.w)};
+      *(f16x4*)(xrow + db * 32 + 8 * gi) = hv;
+    }
+  part += other_half(part);
+  if (half == 0) no.ss[hr * no.ss_stride + h] = part;
+}
+
 template <int DH, bool NS, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   constexpr int KROW = DH * 2;                // bytes per K row (64 or 128)
@@ -225,6 +299,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
       dma16(vbase + (long)t0 * 2 + v_off[i], (lds_void*)(sb + K_BYTES + (wave * V_INSTR + i) * 1024));
   };
 
+  constexpr bool EARLY_G = NW <= 2;
+  OutRow<DH> orow;
+  if (q_ok) out_row_load<DH, EARLY_G>(p, seg, h, qi, orow);
+
   const int t_first = (key_lo / KT) * KT;
   const int ntiles = key_hi > t_first ? (key_hi - t_first + KT - 1) / KT : 0;
 #pragma unroll
@@ -289,21 +367,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
 
   const float l_tot = st.l + __shfl_xor(st.l, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_ok) {
-    float* rrow = p.res + seg * p.res_seg_stride + (p.res_row_base + qi) * p.res_row_stride + h * DH;
-#pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        float4* dst = (float4*)(rrow + db * 32 + 8 * gi + half * 4);
-        float4 r = *dst;
-        r.x += st.o[db][4 * gi + 0] * inv;
-        r.y += st.o[db][4 * gi + 1] * inv;
-        r.z += st.o[db][4 * gi + 2] * inv;
-        r.w += st.o[db][4 * gi + 3] * inv;
-        *dst = r;
-      }
-  }
+  if (q_ok) out_row_store<DH, EARLY_G>(p, seg, h, qi, orow, st.o, inv);
 }
 
 // S-token attention with the keys of one 32-query block split over KS waves: wave w takes
@@ -361,6 +425,8 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   const int t_first = (key_lo / KT) * KT;
   const int ntiles = key_hi > t_first ? (key_hi - t_first + KT - 1) / KT : 0;
   const int n_my = wave < ntiles ? (ntiles - wave + KS - 1) / KS : 0;
+  OutRow<DH> orow;  // wave 0 writes the merged rows
+  if (wave == 0 && q_ok) out_row_load<DH, true>(p, seg, h, qi, orow);
   const char* kbase = (const char*)(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride);
   const char* vbase = (const char*)(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride);
   char* ring = smem + wave * 2 * STAGE;
@@ -426,28 +492,17 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
       for (int j = 0; j < 16; ++j) o[db][j] += src[128 + (db * 16 + j) * 64 + lane] * f;
   }
   const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
-  float* rrow = p.res + seg * p.res_seg_stride + (p.res_row_base + qi) * p.res_row_stride + h * DH;
-#pragma unroll
-  for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      float4* dst = (float4*)(rrow + db * 32 + 8 * gi + half * 4);
-      float4 r = *dst;
-      r.x += o[db][4 * gi + 0] * inv;
-      r.y += o[db][4 * gi + 1] * inv;
-      r.z += o[db][4 * gi + 2] * inv;
-      r.w += o[db][4 * gi + 3] * inv;
-      *dst = r;
-    }
+  out_row_store<DH, true>(p, seg, h, qi, orow, o, inv);
 }
 
-// Zero the K rows and V^T columns [from, cap) of every (user, head) block, so
-// that key tiles reaching past the filled length read finite values.
-__global__ void cache_clear_tail_kernel(__bf16* k, __bf16* vt, int blocks, int dh, int cap, int from) {
-  const int b = blockIdx.y;
+// Zero the K rows and V^T columns [from, cap) of every (user, head) block of every layer
+// (blockIdx.z), so that key tiles reaching past the filled length read finite values.
+__global__ void cache_clear_tail_kernel(ClearTailParams p) {
+  const int l = blockIdx.z, b = blockIdx.y;
+  const int cap = p.cap[l], from = p.from[l], dh = p.dh;
   const int n = cap - from;
-  __bf16* kb = k + (long)b * cap * dh;
-  __bf16* vb = vt + (long)b * dh * cap;
+  __bf16* kb = p.k[l] + (long)b * cap * dh;
+  __bf16* vb = p.vt[l] + (long)b * dh * cap;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n * dh; i += gridDim.x * blockDim.x) {
     kb[(long)from * dh + i] = (__bf16)0.f;
     const int r = i / n, c = i - r * n;
@@ -492,12 +547,16 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
   return hipGetLastError();
 }
 
-hipError_t launch_cache_clear_tail(__bf16* k, __bf16* vt, int blocks, int dh, int cap, int from, hipStream_t s) {
-  if (from >= cap || blocks <= 0) return hipSuccess;
-  const int n = (cap - from) * dh;
-  int gx = (n + 255) / 256;
+hipError_t launch_cache_clear_tail(const ClearTailParams& p, hipStream_t s) {
+  if (p.n_layers <= 0 || p.blocks <= 0) return hipSuccess;
+  if (p.n_layers > ONETRANS_CLEAR_MAX_LAYERS) return hipErrorInvalidValue;
+  int widest = 0;
+  for (int l = 0; l < p.n_layers; ++l)
+    if (p.cap[l] - p.from[l] > widest) widest = p.cap[l] - p.from[l];
+  if (widest <= 0) return hipSuccess;
+  int gx = (widest * p.dh + 255) / 256;
   if (gx > 64) gx = 64;
-  hipLaunchKernelGGL(cache_clear_tail_kernel, dim3(gx, blocks), dim3(256), 0, s, k, vt, blocks, dh, cap, from);
+  hipLaunchKernelGGL(cache_clear_tail_kernel, dim3(gx, p.blocks, p.n_layers), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

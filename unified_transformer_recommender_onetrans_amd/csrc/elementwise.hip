@@ -23,46 +23,62 @@ __global__ void bf16_to_f16_kernel(const uint16_t* __restrict__ src, _Float16* _
   }
 }
 
-__global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, float* __restrict__ dst, long n) {
-  const long i0 = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
-  if (i0 + 8 <= n) {
-    const uint4 v = *(const uint4*)(src + i0);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float4 a, b;
-    a.x = __builtin_bit_cast(float, w[0] << 16); a.y = __builtin_bit_cast(float, w[0] & 0xFFFF0000u);
-    a.z = __builtin_bit_cast(float, w[1] << 16); a.w = __builtin_bit_cast(float, w[1] & 0xFFFF0000u);
-    b.x = __builtin_bit_cast(float, w[2] << 16); b.y = __builtin_bit_cast(float, w[2] & 0xFFFF0000u);
-    b.z = __builtin_bit_cast(float, w[3] << 16); b.w = __builtin_bit_cast(float, w[3] & 0xFFFF0000u);
-    *(float4*)(dst + i0) = a;
-    *(float4*)(dst + i0 + 4) = b;
-  } else {
-    for (long i = i0; i < n; ++i) dst[i] = __builtin_bit_cast(float, (uint32_t)src[i] << 16);
+// One wave per input row: bf16 -> fp32 residual, the first norm's operand x * g (fp16) and
+// the row's sum of squares (slot 0). 8 elements per lane and chunk, d <= 1024.
+__global__ __launch_bounds__(256) void input_rows_kernel(InputParams p) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.n_rows) return;
+  const int u = row / p.rows_per_seg, t = row - u * p.rows_per_seg;
+  bool valid = true;
+  if (p.s_lens) {
+    int len = p.s_lens[u];
+    len = len < 0 ? 0 : (len > p.rows_per_seg ? p.rows_per_seg : len);
+    const int vf = p.rows_per_seg - len;
+    if (t == 0 && lane == 0) p.valid_from[u] = vf;
+    valid = t >= vf;
   }
-}
-
-// S-token input rows -> fp32 residual; padding slots (before s_len - len_u) become 0.
-// One thread per 8 elements of a row; also records the user's first valid slot.
-__global__ void s_input_kernel(const uint16_t* __restrict__ tok, const int* __restrict__ s_lens,
-                               float* __restrict__ x, int* __restrict__ valid_from, int s_len, int d) {
-  const int u = blockIdx.y;
-  const long row = (long)blockIdx.x;  // slot
-  int len = s_lens[u];
-  len = len < 0 ? 0 : (len > s_len ? s_len : len);
-  const int vf = s_len - len;
-  if (row == 0 && threadIdx.x == 0) valid_from[u] = vf;
-  const long base = ((long)u * s_len + row) * d;
-  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    if (row >= vf) {
-      const uint4 v = *(const uint4*)(tok + base + c);
-      a.x = __builtin_bit_cast(float, v.x << 16); a.y = __builtin_bit_cast(float, v.x & 0xFFFF0000u);
-      a.z = __builtin_bit_cast(float, v.y << 16); a.w = __builtin_bit_cast(float, v.y & 0xFFFF0000u);
-      b.x = __builtin_bit_cast(float, v.z << 16); b.y = __builtin_bit_cast(float, v.z & 0xFFFF0000u);
-      b.z = __builtin_bit_cast(float, v.w << 16); b.w = __builtin_bit_cast(float, v.w & 0xFFFF0000u);
+  const long base = (long)row * p.d;
+  const NormOut& no = p.nout;
+  const float* gain = no.gain + (long)(row % p.P) * no.gain_group_stride;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = (lane + 64 * i) * 8;
+    if (c >= p.d) break;
+    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+    if (no.xg) {  // before the stores: a later wait for them would also wait for the stores
+      g0 = *(const float4*)(gain + c);
+      g1 = *(const float4*)(gain + c + 4);
     }
-    *(float4*)(x + base + c) = a;
-    *(float4*)(x + base + c + 4) = b;
+    float v[8];
+    if (valid) {
+      const uint4 w = *(const uint4*)(p.tok + base + c);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __builtin_bit_cast(float, ws[j] << 16);
+        v[2 * j + 1] = __builtin_bit_cast(float, ws[j] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    }
+    *(float4*)(p.x + base + c) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(p.x + base + c + 4) = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+    if (no.xg) {
+      typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+      const f16x8 o = {(_Float16)(v[0] * g0.x), (_Float16)(v[1] * g0.y), (_Float16)(v[2] * g0.z),
+                       (_Float16)(v[3] * g0.w), (_Float16)(v[4] * g1.x), (_Float16)(v[5] * g1.y),
+                       (_Float16)(v[6] * g1.z), (_Float16)(v[7] * g1.w)};
+      *(f16x8*)(no.xg + base + c) = o;
+    }
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if (no.xg && lane == 0) no.ss[(long)row * no.ss_stride] = ss;
 }
 
 __global__ void copy_rows_kernel(const float* __restrict__ src, long src_seg_stride, float* __restrict__ dst,
@@ -83,93 +99,7 @@ __global__ void cache_read_kernel(const __bf16* __restrict__ k, const __bf16* __
   }
 }
 
-// One wave per row: sum of squares over d (lane-strided, coalesced), wave
-// reduction, then the scaled row written as fp16.
-__global__ __launch_bounds__(256) void rmsnorm_f16_kernel(NormParams p) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int g = blockIdx.y;
-  if (row >= p.M) return;
-  const RowMap& rm = p.rm;
-  const int seg = row / rm.rows_per_seg, t = row - seg * rm.rows_per_seg;
-  const float* src = p.res + (long)seg * rm.res_seg_stride + (rm.res_row_base + t) * rm.res_row_stride +
-                     (long)g * rm.res_group_stride;
-  const float* gain = p.gain + (long)g * p.gain_group_stride;
-  _Float16* dst = p.out + (((long)seg * rm.rows_per_seg + t) * rm.row_mult + g) * p.d;
-  constexpr int MAXE = 16;  // d <= 1024
-  float v[MAXE];
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < MAXE; ++i) {
-    const int c = lane + 64 * i;
-    v[i] = c < p.d ? src[c] : 0.f;
-    ss += v[i] * v[i];
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-  const float r = 1.0f / sqrtf(ss / (float)p.d + p.eps);
-#pragma unroll
-  for (int i = 0; i < MAXE; ++i) {
-    const int c = lane + 64 * i;
-    if (c < p.d) dst[c] = (_Float16)(v[i] * r * gain[c]);
-  }
-}
-
-// Two rows per wave (32 lanes each), NV float4 per lane (d = 128 * NV): 16-byte loads,
-// a 32-lane reduction and 8-byte fp16 stores. Flattened row f = row * groups + group,
-// so consecutive waves walk memory in order for candidate-major NS rows.
-template <int NV>
-__global__ __launch_bounds__(256) void rmsnorm_f16_v4_kernel(NormParams p) {
-  const int lane = threadIdx.x & 63, l32 = lane & 31;
-  const long f = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
-  if (f >= (long)p.M * p.groups) return;  // the two halves never exchange data
-  const int row = (int)(f / p.groups), g = (int)(f - (long)row * p.groups);
-  const RowMap& rm = p.rm;
-  const int seg = row / rm.rows_per_seg, t = row - seg * rm.rows_per_seg;
-  const float4* src = (const float4*)(p.res + (long)seg * rm.res_seg_stride + (rm.res_row_base + t) * rm.res_row_stride +
-                                      (long)g * rm.res_group_stride);
-  const float4* gain = (const float4*)(p.gain + (long)g * p.gain_group_stride);
-  _Float16* dst = p.out + (((long)seg * rm.rows_per_seg + t) * rm.row_mult + g) * p.d;
-  float4 v[NV];
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    v[i] = src[l32 + 32 * i];
-    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
-  }
-#pragma unroll
-  for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-  const float r = 1.0f / sqrtf(ss / (float)p.d + p.eps);
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const float4 gv = gain[l32 + 32 * i];
-    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-    const f16x4 o = {(_Float16)(v[i].x * r * gv.x), (_Float16)(v[i].y * r * gv.y), (_Float16)(v[i].z * r * gv.z),
-                     (_Float16)(v[i].w * r * gv.w)};
-    *(f16x4*)(dst + 4 * (l32 + 32 * i)) = o;
-  }
-}
-
 }  // namespace
-
-hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) {
-  if (p.M <= 0 || p.groups <= 0) return hipSuccess;
-  const long rows = (long)p.M * p.groups;
-  const dim3 grid((unsigned)((rows + 7) / 8));
-  switch (p.d % 128 == 0 ? p.d / 128 : 0) {
-    case 1: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<1>, grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<2>, grid, dim3(256), 0, s, p); break;
-    case 3: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<3>, grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<4>, grid, dim3(256), 0, s, p); break;
-    case 5: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<5>, grid, dim3(256), 0, s, p); break;
-    case 6: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<6>, grid, dim3(256), 0, s, p); break;
-    case 7: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<7>, grid, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(rmsnorm_f16_v4_kernel<8>, grid, dim3(256), 0, s, p); break;
-    default:  // d not a multiple of 128: one row per wave
-      hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((p.M + 3) / 4, p.groups), dim3(256), 0, s, p);
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
@@ -178,18 +108,10 @@ hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, long n, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, long n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const long threads = (n + 7) / 8;
-  hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, src, dst, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_s_input(const uint16_t* tok, const int* s_lens, float* x, int* valid_from, int B, int s_len, int d,
-                          hipStream_t s) {
-  if (B <= 0) return hipSuccess;
-  const int threads = d / 8 < 64 ? 64 : (d / 8 > 128 ? 128 : d / 8);
-  hipLaunchKernelGGL(s_input_kernel, dim3(s_len, B), dim3(threads), 0, s, tok, s_lens, x, valid_from, s_len, d);
+hipError_t launch_input_rows(const InputParams& p, hipStream_t s) {
+  if (p.n_rows <= 0) return hipSuccess;
+  if (p.d % 8 != 0 || p.d > 1024 || p.P < 1 || p.rows_per_seg < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(input_rows_kernel, dim3((unsigned)((p.n_rows + 3) / 4)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

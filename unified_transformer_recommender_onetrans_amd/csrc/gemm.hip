@@ -2,12 +2,14 @@
 //
 // One kernel template covers the linear maps of a layer (agihunt.info OneTrans
 // summary, "method": shared S-token QKV/FFN, private per-NS-position QKV/FFN):
-//   GEMM_QKV      : A = RMSNorm'd rows (fp16), B = W_QKV [3d][d];
-//                   epilogue writes bf16 Q / K / V (V transposed for the S cache)
-//   GEMM_FFN_UP   : A = RMSNorm'd rows (fp16), B = W1 [F][d];
-//                   epilogue GELU -> fp16 hidden rows
-//   GEMM_FFN_DOWN : A = fp16 hidden rows, B = W2 [d][F];
-//                   epilogue adds into the fp32 residual rows in place
+//   GEMM_QKV      : A = x * g rows (fp16), B = W_QKV [3d][d]; epilogue scales the row by
+//                   its RMSNorm factor r and writes bf16 Q / K / V (V transposed for
+//                   the S cache)
+//   GEMM_FFN_UP   : A = x * g rows (fp16), B = W1 [F][d]; epilogue GELU(r * acc) ->
+//                   fp16 hidden rows
+//   GEMM_FFN_DOWN : A = fp16 hidden rows, B = W2 [d][F]; epilogue adds into the fp32
+//                   residual rows in place and writes the next norm's x * g rows and
+//                   partial sums of squares (the deferred RMSNorm described with NormOut)
 // A group is one NS position (private weights) or the shared S weights.
 //
 // Persistent schedule, one workgroup of 8 waves per CU. The work list (BM x BN
@@ -29,11 +31,11 @@
 // 16-byte chunks XOR-swizzled by row, so the MFMA fragment reads are free of bank
 // conflicts on the 64-bank LDS.
 //
-// MFMA: v_mfma_f32_32x32x16_f16; the compute waves form a WM x (4/WM) grid, each
-// owning a block of 32x32 accumulators. A lane ends up holding one output column
-// and groups of four consecutive rows, so each epilogue store instruction writes
-// 32 consecutive columns (64 or 128 contiguous bytes) of two rows. E4M3 weights
-// are decoded to fp16 exactly in registers after the LDS read.
+// MFMA: v_mfma_f32_32x32x16_f16 with the weight fragment as the first operand; the
+// compute waves form a WM x (4/WM) grid, each owning a block of 32x32 accumulators. A
+// lane ends up holding one output row and groups of four consecutive columns, so the
+// epilogue writes 16 contiguous bytes per lane and instruction. E4M3 weights are
+// decoded to fp16 exactly in registers after the LDS read.
 #include "internal.h"
 
 namespace onetrans {
@@ -126,7 +128,6 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
   constexpr int A_CPR = AROW / 16, B_CPR = BROW / 16;      // 16-byte chunks per row
   static_assert(WM * WN == 4 && TM % 32 == 0 && TN % 32 == 0, "wave grid");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "tile shape");
-  constexpr bool STAGED = KIND != GEMM_FFN_DOWN;  // 16-bit outputs written from registers
   static_assert(STAGES >= 2 && STAGES * STAGE <= 159 * 1024, "LDS");
   static_assert(PT * (STAGES - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
@@ -206,6 +207,51 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
+    // deferred RMSNorm (QKV, FFN up): load this item's row partials now, so that they have
+    // arrived by the epilogue. Chunks of four partials alternate between the half-waves;
+    // chunks 0-3 (16 partials) are held through the k-loop, any beyond load in the epilogue.
+    const float* ss_rows[MI];
+    float4 ss_raw[MI][2];
+    if (KIND != GEMM_FFN_DOWN && p.ss_in) {
+      const int w = ib + t * nx;
+      const int mt = w % n_tiles_m, g = w / (n_tiles_m * n_tiles_n);
+      const int last_chunk = p.ss_stride / 4 - 1;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = min(mt * BM + wm * TM + mi * 32 + (lane & 31), M - 1);
+        int seg, tt;
+        split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
+        ss_rows[mi] = p.ss_in + hid_row(rm, seg, tt, g) * p.ss_stride;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) ss_raw[mi][j] = *(const float4*)(ss_rows[mi] + 4 * min(2 * j + (lane >> 5), last_chunk));
+      }
+    }
+    // FFN down with few accumulator blocks per wave: load the residual rows of this item now
+    // as well (each element belongs to one item, so nothing writes them in between)
+    constexpr bool X_EARLY = KIND == GEMM_FFN_DOWN && MI * NI <= 3;
+    float4 x_pre[X_EARLY ? MI : 1][X_EARLY ? NI : 1][4];
+    if constexpr (X_EARLY) {
+      const int w = ib + t * nx;
+      const int mt = w % n_tiles_m, nt = (w / n_tiles_m) % n_tiles_n, g = w / (n_tiles_m * n_tiles_n);
+      const int col = nt * BN + wn * TN + 4 * (lane >> 5);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = min(mt * BM + wm * TM + mi * 32 + (lane & 31), M - 1);
+        int seg, tt;
+        split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
+        const float* rrow = p.res_out + res_row_off(rm, seg, tt, g) + col;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x_pre[mi][ni][q] = *(const float4*)(rrow + ni * 32 + 8 * q);
+      }
+    }
+    // the partials of chunk c4 that exist (the rest of a row's slots may hold stale data)
+    auto chunk_sum = [&](float4 v, int c4) {
+      const int b = 4 * c4, n = p.ss_parts;
+      return (b < n ? v.x : 0.f) + (b + 1 < n ? v.y : 0.f) + (b + 2 < n ? v.z : 0.f) + (b + 3 < n ? v.w : 0.f);
+    };
+
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
       const int s = t * nk + kt;
@@ -232,85 +278,86 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = STAGED ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b[ni], a[mi], acc[mi][ni], 0, 0, 0)
-                                 : __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[ni], a[mi], acc[mi][ni], 0, 0, 0);
       }
     }
 
-    // ---- epilogue. Lane holds column (lane % 32) of each 32x32 block and, in
-    // registers 4q..4q+3, rows 8q + 4*(lane/32) + 0..3: a store instruction covers
-    // 32 consecutive columns of two rows. Addresses: one base per group of four rows,
-    // then a constant step per row (integer multiplies run at a quarter of the VALU rate).
+    // ---- epilogue. With the weight fragment first in the MFMA, lane holds output row
+    // (lane % 32) of each 32x32 block and, in registers 4q..4q+3, columns
+    // 8q + 4*(lane/32) + 0..3. ----
     const int w = ib + t * nx;
     const int mt = w % n_tiles_m, nt = (w / n_tiles_m) % n_tiles_n, g = w / (n_tiles_m * n_tiles_n);
     const int m0 = mt * BM, n0 = nt * BN;
     const float scale = FP8 ? p.wscale[g * 5 + p.scale_idx0 + n0 / p.scale_col_div] : 1.f;
-    const int col0 = n0 + wn * TN + (lane & 31);     // + ni*32
-    const int row_w = m0 + wm * TM + 4 * (lane >> 5);  // + mi*32 + 8q + e
-    const int rps = rm.rows_per_seg, rmult = rm.row_mult;
-    auto step = [&](int& seg, int& tt) {
-      if (++tt >= rps) { tt = 0; ++seg; }
-    };
-    // visits the (up to) four rows r0..r0+3 of one register group: f(element offset, e, t)
-    auto rows4 = [&](int r0, long rstep, auto&& base_of, auto&& f) {
-      int seg, tt;
-      split_row(r0, rps, inv_rps, seg, tt);
-      if (r0 + 3 < M && tt + 3 < rps) {
-        const long o = base_of(seg, tt);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f(o + e * rstep, e, tt + e);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (r0 + e >= M) break;
-          f(base_of(seg, tt), e, tt);
-          step(seg, tt);
-        }
-      }
-    };
+    const int half = lane >> 5;
+    const int col_l = n0 + wn * TN;                // + ni*32 + 8q + 4*half
+    const int row_l = m0 + wm * TM + (lane & 31);  // + mi*32
     if (KIND == GEMM_FFN_DOWN) {
-      // read-modify-write of the fp32 residual, one 32-row block at a time to bound registers
-      auto base_of = [&](int seg, int tt) { return res_row_off(rm, seg, tt, g) + col0; };
-      const long rstep = rm.res_row_stride;
+      // fp32 residual rows: read-modify-write 16 bytes per (block, register group); then
+      // the next norm's operand x * g and one partial sum of squares per 32 columns
+      const NormOut& no = p.nout;
+      // the gains (the same columns for every row) before any store: a wait for a load
+      // issued after a store also waits for that store
+      float4 gv[NI][4];
+      if (no.xg) {
+        const float* grow = no.gain + (long)g * no.gain_group_stride + col_l + 4 * half;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) gv[ni][q] = *(const float4*)(grow + ni * 32 + 8 * q);
+      }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        float old[4][4][NI];
-        long off[4][4];
+        const int row = row_l + mi * 32;
+        if (row >= M) continue;  // both half-waves hold the same row
+        int seg, tt;
+        split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
+        float* rrow = p.res_out + res_row_off(rm, seg, tt, g) + col_l + 4 * half;
+        float4 x[NI][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r0 = min(row_w + mi * 32 + 8 * q, M - 1);
+        for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) off[q][e] = -1;
-          rows4(r0, rstep, base_of, [&](long o, int e, int) { off[q][e] = o; });
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float* src = p.res_out + (off[q][e] >= 0 ? off[q][e] : off[q][0]);
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) old[q][e][ni] = src[ni * 32];
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (X_EARLY) x[ni][q] = x_pre[mi][ni][q];
+            else x[ni][q] = *(const float4*)(rrow + ni * 32 + 8 * q);
           }
-        }
-        wait_vmcnt<0>();  // the residual rows (and this wave's earlier stores)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (row_w + mi * 32 + 8 * q >= M) continue;
+        for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (off[q][e] < 0 || row_w + mi * 32 + 8 * q + e >= M) continue;
-            float* dst = p.res_out + off[q][e];
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[mi][ni];
+            float4& v = x[ni][q];
+            v.x += a[4 * q + 0] * scale;
+            v.y += a[4 * q + 1] * scale;
+            v.z += a[4 * q + 2] * scale;
+            v.w += a[4 * q + 3] * scale;
+            *(float4*)(rrow + ni * 32 + 8 * q) = v;
+          }
+        if (no.xg) {
+          const long hr = hid_row(rm, seg, tt, g);
+          _Float16* xrow = no.xg + hr * N + col_l + 4 * half;
+          float* srow = no.ss + hr * no.ss_stride + (col_l >> 5);
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) dst[ni * 32] = old[q][e][ni] + acc[mi][ni][4 * q + e] * scale;
+          for (int ni = 0; ni < NI; ++ni) {
+            float part = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 v = x[ni][q], gg = gv[ni][q];
+              part += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+              const f16x4 o = {(_Float16)(v.x * gg.x), (_Float16)(v.y * gg.y), (_Float16)(v.z * gg.z),
+                               (_Float16)(v.w * gg.w)};
+              *(f16x4*)(xrow + ni * 32 + 8 * q) = o;
+            }
+            part += other_half(part);
+            if (half == 0) srow[ni] = part;
           }
         }
       }
     } else {
-      // ---- 16-bit outputs (Q / K / V, GELU hidden rows), straight from registers. With the
-      // weight fragment first, lane holds output row (lane % 32) of each 32x32 block and, in
-      // registers 4q..4q+3, columns 8q + 4*(lane/32) + 0..3. Packed to 16-bit pairs, groups
-      // q and q+1 trade halves across the two half-waves (v_permlane32_swap), after which a
-      // lane holds 8 consecutive columns of one group: one 16-byte store each. ----
-      const int half = lane >> 5;
-      const int col_l = n0 + wn * TN;          // + ni*32 + 8*(qq + half)
-      const int row_l = m0 + wm * TM + (lane & 31);  // + mi*32
+      // ---- 16-bit outputs (Q / K / V, GELU hidden rows), straight from registers. Packed
+      // to 16-bit pairs, groups q and q+1 trade halves across the two half-waves
+      // (v_permlane32_swap), after which a lane holds 8 consecutive columns of one group:
+      // one 16-byte store each. Rows are scaled by the deferred RMSNorm factor. ----
       auto pack2 = [&](float x, float y) -> uint32_t {
         if (KIND == GEMM_FFN_UP) {
           const _Float16 hx = (_Float16)x, hy = (_Float16)y;
@@ -319,16 +366,30 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
         const __bf16 bx = (__bf16)x, by = (__bf16)y;
         return (uint32_t)__builtin_bit_cast(uint16_t, bx) | ((uint32_t)__builtin_bit_cast(uint16_t, by) << 16);
       };
-      auto val = [&](float x) { return KIND == GEMM_FFN_UP ? gelu_as(x * scale) : x * scale; };
       const int typ = KIND == GEMM_QKV ? n0 / p.d : 0;
       const bool vt_mode = KIND == GEMM_QKV && typ == 2 && p.vt != nullptr;
       const int dsh = p.dh == 64 ? 6 : 5;
+      // every row factor before the first store: on gfx9 a wait for a load issued
+      // after a store also waits for that store
+      float srow[MI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        srow[mi] = scale;
+        if (p.ss_in) {
+          float sum = chunk_sum(ss_raw[mi][0], half) + chunk_sum(ss_raw[mi][1], 2 + half);
+          for (int c4 = 4 + half; 4 * c4 < p.ss_parts; c4 += 2) sum += chunk_sum(*(const float4*)(ss_rows[mi] + 4 * c4), c4);
+          sum += other_half(sum);
+          srow[mi] *= 1.0f / sqrtf(sum / (float)K + p.eps);
+        }
+      }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int row = row_l + mi * 32;
         if (row >= M) continue;
         int seg, tt;
         split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
+        const float sr = srow[mi];
+        auto val = [&](float x) { return KIND == GEMM_FFN_UP ? gelu_as(x * sr) : x * sr; };
         if (vt_mode) {
           // transposed V: lanes hold 32 consecutive key slots of each column
           __bf16* base = p.vt + seg * p.kv_seg_stride + p.kv_slot_base + (long)tt * rm.row_mult + g;
@@ -340,7 +401,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
               for (int e = 0; e < 4; ++e) {
                 const int cc = col_l - typ * p.d + ni * 32 + 8 * q + 4 * half + e;
                 base[(cc >> dsh) * p.kv_head_stride + (long)(cc & (p.dh - 1)) * p.kv_cap] =
-                    (__bf16)(acc[mi][ni][4 * q + e] * scale);
+                    (__bf16)val(acc[mi][ni][4 * q + e]);
               }
           continue;
         }

@@ -27,6 +27,14 @@ __device__ __forceinline__ float gelu_as(float x) {
   return fmaf(hx, __builtin_copysignf(erf_abs, x), hx);
 }
 
+// The value that lane l ^ 32 holds (v_permlane32_swap: no LDS traffic). Both lanes of a
+// pair must be active.
+__device__ __forceinline__ float other_half(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
 // lane i's bytes land at lds + 16 * i. The 16-byte form exists only on gfx950, so the
 // host compilation pass, which never runs device code, does not see the builtin.
@@ -51,11 +59,32 @@ struct RowMap {
   long res_seg_stride, res_row_base, res_row_stride, res_group_stride;
 };
 
+// Deferred RMSNorm. RMSNorm(x) W = r (x * g) W with r = 1 / sqrt(mean(x^2) + eps), one
+// number per row, so the norm needs no pass of its own: whichever kernel writes residual
+// rows (input conversion, attention, FFN down) also writes the operand of the next linear
+// map, fp16 x * g (g: the gain of the norm that comes next), and partial sums of x^2 over
+// the columns it owns; the GEMM that reads the operand sums the row's partials and scales
+// its output row by r. Partials sit in rows of `ss_stride` floats (hidden-row addressing
+// like the operand): FFN down writes slot c / 32 for columns c .. c + 31, attention slot h
+// for head h, input conversion slot 0 for the whole row.
+// Fixed slots keep the sums deterministic: every output is a function of its own row.
+struct NormOut {
+  _Float16* xg;              // operand rows [hidden row][d]; NULL: no norm follows
+  const float* gain;         // gain row of group g at gain + g * gain_group_stride
+  long gain_group_stride;
+  float* ss;                 // partials [hidden row][ss_stride]
+  int ss_stride;
+};
+__host__ __device__ constexpr int ss_stride_for(int d) { return ((d / 32 + 3) / 4) * 4; }
+
 struct GemmParams {
   int M, N, K, groups;
   RowMap rm;
-  // A operand: fp16 rows at a_in + hidden_row * K (RMSNorm'd activations or FFN hidden rows)
+  // A operand: fp16 rows at a_in + hidden_row * K (x * g rows or FFN hidden rows)
   const _Float16* a_in;
+  // QKV / FFN up: deferred RMSNorm of the A rows, r from ss_in[hidden row][0 .. ss_parts)
+  // (ss_parts <= 32, rows of ss_stride floats); NULL: no row scale
+  const float* ss_in; int ss_parts, ss_stride; float eps;
   // B operand: weights [N][K] (fp16 or E4M3FN codes), per-group stride in elements
   const void* w;
   long w_group_stride;
@@ -69,8 +98,9 @@ struct GemmParams {
   __bf16* k; __bf16* vt; __bf16* v; long kv_seg_stride, kv_head_stride; int kv_cap, kv_slot_base;
   // epilogue: GELU into hidden rows (ld = N)
   _Float16* hid_out;
-  // epilogue: residual add (residual addressing)
+  // epilogue: residual add (residual addressing), then the next norm's operand (FFN down)
   float* res_out;
+  NormOut nout;
 };
 
 enum GemmKind { GEMM_QKV = 0, GEMM_FFN_UP = 1, GEMM_FFN_DOWN = 2 };
@@ -93,32 +123,39 @@ struct AttnParams {
   // NS only: own keys and values of the candidates, row-major kn, vn [H][nq][dh]; P NS tokens each
   const __bf16* kn; const __bf16* vn; long kn_head_stride; int P;
   float scale_log2;  // log2(e) / sqrt(dh)
+  // the FFN norm's operand: hidden row seg * nq + i, gain group i % P, partial slot h
+  NormOut nout;
 };
 
 hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s);
 
-// Zeroes cache slots [from, cap) of `blocks` (user, head) blocks: K [blocks][cap][dh] and
-// V^T [blocks][dh][cap]. Key tiles that reach past the filled length then read zeros.
-hipError_t launch_cache_clear_tail(__bf16* k, __bf16* vt, int blocks, int dh, int cap, int from, hipStream_t s);
-
-// RMSNorm of M residual rows per group (residual addressing) into fp16 rows at
-// out + hidden_row * d, with the group's gain row: x / sqrt(mean(x^2) + eps) * g.
-struct NormParams {
-  int M, groups, d;
-  RowMap rm;
-  const float* res;
-  const float* gain;
-  long gain_group_stride;
-  float eps;
-  _Float16* out;
+// Zeroes cache slots [from[l], cap[l]) of `blocks` (user, head) blocks of every layer l in
+// one launch: K [blocks][cap][dh] and V^T [blocks][dh][cap]. Key tiles that reach past
+// the filled length then read zeros.
+constexpr int ONETRANS_CLEAR_MAX_LAYERS = 16;
+struct ClearTailParams {
+  __bf16* k[ONETRANS_CLEAR_MAX_LAYERS];
+  __bf16* vt[ONETRANS_CLEAR_MAX_LAYERS];
+  int cap[ONETRANS_CLEAR_MAX_LAYERS], from[ONETRANS_CLEAR_MAX_LAYERS];
+  int n_layers, blocks, dh;
 };
-hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
+hipError_t launch_cache_clear_tail(const ClearTailParams& p, hipStream_t s);
+
+// Input rows (bf16) -> fp32 residual rows plus the first norm's operand and one partial
+// per row. Row i of user i / rows_per_seg; with s_lens (S prefill) the first
+// rows_per_seg - len_u rows of user u are padding and become zero, and valid_from[u]
+// records the first valid one. Gain group of row i: i % P.
+struct InputParams {
+  const uint16_t* tok;
+  const int* s_lens; int* valid_from;
+  int n_rows, rows_per_seg, d, P;
+  float* x;
+  NormOut nout;
+};
+hipError_t launch_input_rows(const InputParams& p, hipStream_t s);
 
 // Elementwise helpers.
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, long n, hipStream_t s);
-hipError_t launch_s_input(const uint16_t* tok, const int* s_lens, float* x, int* valid_from,
-                          int B, int s_len, int d, hipStream_t s);
-hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, long n, hipStream_t s);
 hipError_t launch_copy_rows_f32(const float* src, long src_seg_stride, float* dst, long dst_seg_stride,
                                 long row_elems, int n_seg, hipStream_t s);
 hipError_t launch_cache_read(const __bf16* k, const __bf16* vt, int H, int dh, int cap, int rows,

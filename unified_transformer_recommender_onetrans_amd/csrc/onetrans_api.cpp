@@ -105,30 +105,37 @@ size_t cache_layout(const Shape& s, int B, size_t* k_off, size_t* v_off) {
   return off;
 }
 
-struct PrefillWs { size_t x, q, xn, hid, total; };
+// Every path keeps, per activation row, the fp16 operand of the next linear map (xn: x * g
+// or the norm-free FFN hidden row) and the row's partial sums of squares (ss, deferred
+// RMSNorm: ss_stride_for(d) floats per row).
+struct PrefillWs { size_t x, q, xn, ss, hid, total; };
 PrefillWs prefill_ws(const Shape& s, int B) {
   PrefillWs w;
   size_t off = 0;
-  w.x = off; off = align_up(off + (size_t)B * s.s_len * s.d * 4);
+  const size_t rows = (size_t)B * s.s_len;
+  w.x = off; off = align_up(off + rows * s.d * 4);
   w.q = off; off = align_up(off + (size_t)B * s.H * s.q[0] * s.dh * 2);
-  w.xn = off; off = align_up(off + (size_t)B * s.s_len * s.d * 2);
+  w.xn = off; off = align_up(off + rows * s.d * 2);
+  w.ss = off; off = align_up(off + rows * ss_stride_for(s.d) * 4);
   w.hid = off; off = align_up(off + (size_t)B * s.q[0] * s.F * 2);
   w.total = off;
   return w;
 }
 
-struct AppendWs { size_t q, xn, hid, total; };
+struct AppendWs { size_t q, xn, ss, hid, total; };
 AppendWs append_ws(const Shape& s, int B, int m) {
   AppendWs w;
   size_t off = 0;
+  const size_t rows = (size_t)B * m;
   w.q = off; off = align_up(off + (size_t)B * s.H * m * s.dh * 2);
-  w.xn = off; off = align_up(off + (size_t)B * m * s.d * 2);
-  w.hid = off; off = align_up(off + (size_t)B * m * s.F * 2);
+  w.xn = off; off = align_up(off + rows * s.d * 2);
+  w.ss = off; off = align_up(off + rows * ss_stride_for(s.d) * 4);
+  w.hid = off; off = align_up(off + rows * s.F * 2);
   w.total = off;
   return w;
 }
 
-struct ScoreWs { size_t qn, kn, vn, xn, hid, total; };
+struct ScoreWs { size_t qn, kn, vn, xn, ss, hid, total; };
 ScoreWs score_ws(const Shape& s, int C) {
   ScoreWs w;
   size_t off = 0;
@@ -137,6 +144,7 @@ ScoreWs score_ws(const Shape& s, int C) {
   w.kn = off; off = align_up(off + rows * s.d * 2);
   w.vn = off; off = align_up(off + rows * s.d * 2);
   w.xn = off; off = align_up(off + rows * s.d * 2);
+  w.ss = off; off = align_up(off + rows * ss_stride_for(s.d) * 4);
   w.hid = off; off = align_up(off + rows * s.F * 2);
   w.total = off;
   return w;
@@ -150,6 +158,8 @@ GemmParams base_gemm(const Shape& s) {
 
   g.scale_col_div = 1 << 30;
   g.groups = 1;
+  g.ss_stride = ss_stride_for(s.d);
+  g.eps = s.eps;
   return g;
 }
 
@@ -212,16 +222,18 @@ struct SLayerArgs {
   __bf16* k; __bf16* vt; int cap, slot_base, n_keys, key_pos0;
   const int* valid_from;
   __bf16* qbuf; _Float16* xn; _Float16* hid;
+  float* ss; int ss_parts;   // the layer input's partial sums (deferred RMSNorm) and their count
+  const float* next_ga;      // attention-norm gain of the next layer; NULL after the last
 };
 
-int run_norm(const Shape& s, int fam, int M, int groups, const RowMap& rm, const float* res, const float* gain,
-             long gain_group_stride, _Float16* out, hipStream_t st) {
-  NormParams np;
-  np.M = M; np.groups = groups; np.d = s.d; np.rm = rm; np.res = res; np.gain = gain;
-  np.gain_group_stride = gain_group_stride; np.eps = s.eps; np.out = out;
-  FamilyTimer t(fam, st);
-  OT_HIP(launch_rmsnorm(np, st), "RMSNorm launch");
-  return ONETRANS_OK;
+NormOut norm_out(const Shape& s, _Float16* xg, const float* gain, long gain_group_stride, float* ss) {
+  NormOut n;
+  n.xg = gain ? xg : nullptr;
+  n.gain = gain;
+  n.gain_group_stride = gain_group_stride;
+  n.ss = ss;
+  n.ss_stride = ss_stride_for(s.d);
+  return n;
 }
 
 int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SLayerArgs& a, hipStream_t st) {
@@ -229,12 +241,11 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
   RowMap all{a.rows, 1, a.x_seg_stride, a.x_row_base, d, 0};
   RowMap tail{a.q, 1, a.x_seg_stride, a.x_row_base + (a.rows - a.q), d, 0};
 
-  int rc = run_norm(s, ONETRANS_K_S_NORM, a.B * a.rows, 1, all, a.x, (const float*)(pk + lo.s_ga), 0, a.xn, st);
-  if (rc) return rc;
   GemmParams g = base_gemm(s);
   g.M = a.B * a.rows; g.N = 3 * s.d; g.K = s.d;
   g.rm = all;
   g.a_in = a.xn;
+  g.ss_in = a.ss; g.ss_parts = a.ss_parts;
   g.w = pk + lo.s_wqkv;
   g.q = a.qbuf; g.q_seg_stride = (long)s.H * a.q * s.dh; g.q_head_stride = (long)a.q * s.dh; g.q_from = a.rows - a.q;
   g.k = a.k; g.vt = a.vt; g.kv_seg_stride = (long)s.H * a.cap * s.dh; g.kv_head_stride = (long)a.cap * s.dh;
@@ -255,17 +266,17 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
   at.valid_from = a.valid_from;
   at.P = 1;
   at.scale_log2 = scale_log2(s);
+  at.nout = norm_out(s, a.xn, (const float*)(pk + lo.s_gf), 0, a.ss);
   {
     FamilyTimer t(ONETRANS_K_S_ATTN, st);
     OT_HIP(launch_attention(false, s.dh, at, a.B, st), "S attention launch");
   }
 
-  rc = run_norm(s, ONETRANS_K_S_NORM, a.B * a.q, 1, tail, a.x, (const float*)(pk + lo.s_gf), 0, a.xn, st);
-  if (rc) return rc;
   GemmParams u = base_gemm(s);
   u.M = a.B * a.q; u.N = s.F; u.K = s.d;
   u.rm = tail;
   u.a_in = a.xn;
+  u.ss_in = a.ss; u.ss_parts = s.H;
   u.w = pk + lo.s_w1;
   u.hid_out = a.hid;
   {
@@ -279,6 +290,7 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
   dn.a_in = a.hid;
   dn.w = pk + lo.s_w2;
   dn.res_out = a.x;
+  dn.nout = norm_out(s, a.xn, a.next_ga, 0, a.ss);
   {
     FamilyTimer t(ONETRANS_K_S_FFN_DOWN, st);
     OT_HIP(launch_gemm(GEMM_FFN_DOWN, false, false, dn, st), "S FFN down launch");
@@ -295,25 +307,28 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
   __bf16* kn = (__bf16*)(ws + w.kn);
   __bf16* vn = (__bf16*)(ws + w.vn);
   _Float16* xn = (_Float16*)(ws + w.xn);
+  float* ss = (float*)(ws + w.ss);
   _Float16* hid = (_Float16*)(ws + w.hid);
   const long d = s.d, P = s.P, rows = (long)C * P;
   const int* vf = (const int*)cache_buf;
   {
+    InputParams ip;
+    memset(&ip, 0, sizeof(ip));
+    ip.tok = ns_tokens; ip.n_rows = (int)rows; ip.rows_per_seg = (int)rows; ip.d = s.d; ip.P = s.P;
+    ip.x = ns_out;
+    ip.nout = norm_out(s, xn, (const float*)(pk + lo[0].ns_ga), d, ss);
     FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
-    OT_HIP(launch_bf16_to_f32(ns_tokens, ns_out, rows * d, st), "NS input conversion launch");
+    OT_HIP(launch_input_rows(ip, st), "NS input conversion launch");
   }
   const RowMap rm{C, s.P, 0, 0, P * d, d};
   for (int l = 0; l < s.L; ++l) {
     const long cap = s.cap[l];
     const int len = s.n[l] + n_appended;
-    {
-      int rc = run_norm(s, ONETRANS_K_NS_NORM, C, s.P, rm, ns_out, (const float*)(pk + lo[l].ns_ga), d, xn, st);
-      if (rc) return rc;
-    }
     GemmParams g = base_gemm(s);
     g.M = C; g.N = 3 * s.d; g.K = s.d; g.groups = s.P;
     g.rm = rm;
     g.a_in = xn;
+    g.ss_in = ss; g.ss_parts = l == 0 ? 1 : s.d / 32;
     g.w = pk + lo[l].ns_wqkv; g.w_group_stride = 3 * d * d;
     g.wscale = (const float*)(pk + lo[l].ns_scale); g.scale_idx0 = 0; g.scale_col_div = s.d;
     g.q = qn; g.q_seg_stride = 0; g.q_head_stride = rows * s.dh; g.q_from = 0;
@@ -337,17 +352,17 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     at.valid_from = vf + user;
     at.kn = kn; at.vn = vn; at.kn_head_stride = rows * s.dh; at.P = s.P;
     at.scale_log2 = scale_log2(s);
+    at.nout = norm_out(s, xn, (const float*)(pk + lo[l].ns_gf), d, ss);
     {
       FamilyTimer t(ONETRANS_K_NS_ATTN, st);
       OT_HIP(launch_attention(true, s.dh, at, 1, st), "NS attention launch");
     }
 
-    int rc = run_norm(s, ONETRANS_K_NS_NORM, C, s.P, rm, ns_out, (const float*)(pk + lo[l].ns_gf), d, xn, st);
-    if (rc) return rc;
     GemmParams u = base_gemm(s);
     u.M = C; u.N = s.F; u.K = s.d; u.groups = s.P;
     u.rm = rm;
     u.a_in = xn;
+    u.ss_in = ss; u.ss_parts = s.H;
     u.w = pk + lo[l].ns_w1; u.w_group_stride = (long)s.F * d;
     u.wscale = (const float*)(pk + lo[l].ns_scale); u.scale_idx0 = 3;
     u.hid_out = hid;
@@ -363,6 +378,7 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     dn.w = pk + lo[l].ns_w2; dn.w_group_stride = d * s.F;
     dn.wscale = (const float*)(pk + lo[l].ns_scale); dn.scale_idx0 = 4;
     dn.res_out = ns_out;
+    dn.nout = norm_out(s, xn, l + 1 < s.L ? (const float*)(pk + lo[l + 1].ns_ga) : nullptr, d, ss);
     {
       FamilyTimer t(ONETRANS_K_NS_FFN_DOWN, st);
       OT_HIP(launch_gemm(GEMM_FFN_DOWN, s.fp8, true, dn, st), "NS FFN down launch");
@@ -377,16 +393,31 @@ int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const u
                  float* s_out, char* ws, hipStream_t st) {
   const PrefillWs w = prefill_ws(s, B);
   float* x = (float*)(ws + w.x);
+  float* ss = (float*)(ws + w.ss);
+  _Float16* xn = (_Float16*)(ws + w.xn);
   int* vf = (int*)cache_buf;
   {
+    InputParams ip;
+    memset(&ip, 0, sizeof(ip));
+    ip.tok = s_tokens; ip.s_lens = s_lens; ip.valid_from = vf;
+    ip.n_rows = B * s.s_len; ip.rows_per_seg = s.s_len; ip.d = s.d; ip.P = 1;
+    ip.x = x;
+    ip.nout = norm_out(s, xn, (const float*)(pk + lo[0].s_ga), 0, ss);
     FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
-    OT_HIP(launch_s_input(s_tokens, s_lens, x, vf, B, s.s_len, s.d, st), "S input conversion launch");
+    OT_HIP(launch_input_rows(ip, st), "S input conversion launch");
   }
-  for (int l = 0; l < s.L; ++l) {
+  {
+    ClearTailParams ct;
+    memset(&ct, 0, sizeof(ct));
+    ct.n_layers = s.L; ct.blocks = B * s.H; ct.dh = s.dh;
+    for (int l = 0; l < s.L; ++l) {
+      ct.k[l] = (__bf16*)(cache_buf + k_off[l]);
+      ct.vt[l] = (__bf16*)(cache_buf + v_off[l]);
+      ct.cap[l] = s.cap[l];
+      ct.from[l] = s.n[l];
+    }
     FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
-    OT_HIP(launch_cache_clear_tail((__bf16*)(cache_buf + k_off[l]), (__bf16*)(cache_buf + v_off[l]), B * s.H, s.dh,
-                                   s.cap[l], s.n[l], st),
-           "cache tail clear launch");
+    OT_HIP(launch_cache_clear_tail(ct, st), "cache tail clear launch");
   }
   for (int l = 0; l < s.L; ++l) {
     SLayerArgs a;
@@ -395,7 +426,9 @@ int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const u
     a.k = (__bf16*)(cache_buf + k_off[l]); a.vt = (__bf16*)(cache_buf + v_off[l]);
     a.cap = s.cap[l]; a.slot_base = 0; a.n_keys = s.n[l]; a.key_pos0 = s.s_len - s.n[l];
     a.valid_from = vf;
-    a.qbuf = (__bf16*)(ws + w.q); a.xn = (_Float16*)(ws + w.xn); a.hid = (_Float16*)(ws + w.hid);
+    a.qbuf = (__bf16*)(ws + w.q); a.xn = xn; a.hid = (_Float16*)(ws + w.hid);
+    a.ss = ss; a.ss_parts = l == 0 ? 1 : s.d / 32;
+    a.next_ga = l + 1 < s.L ? (const float*)(pk + lo[l + 1].s_ga) : nullptr;
     int rc = run_s_layer(s, pk, lo[l], a, st);
     if (rc) return rc;
   }
@@ -579,9 +612,16 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
   cache_layout(s, B, k_off, v_off);
   char* cb = (char*)cache->buf;
   char* ws = (char*)workspace;
+  _Float16* xn = (_Float16*)(ws + w.xn);
+  float* ss = (float*)(ws + w.ss);
   {
+    InputParams ip;
+    memset(&ip, 0, sizeof(ip));
+    ip.tok = new_tokens; ip.n_rows = B * m; ip.rows_per_seg = m; ip.d = s.d; ip.P = 1;
+    ip.x = new_out;
+    ip.nout = norm_out(s, xn, (const float*)((const char*)packed + lo[0].s_ga), 0, ss);
     FamilyTimer t(ONETRANS_K_ELEMENTWISE, stream);
-    OT_HIP(launch_bf16_to_f32(new_tokens, new_out, (long)B * m * s.d, stream), "append input conversion launch");
+    OT_HIP(launch_input_rows(ip, stream), "append input conversion launch");
   }
   for (int l = 0; l < s.L; ++l) {
     const int len = s.n[l] + cache->n_appended;
@@ -591,7 +631,9 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
     a.k = (__bf16*)(cb + k_off[l]); a.vt = (__bf16*)(cb + v_off[l]);
     a.cap = s.cap[l]; a.slot_base = len; a.n_keys = len + m; a.key_pos0 = s.s_len - s.n[l];
     a.valid_from = (const int*)cb;
-    a.qbuf = (__bf16*)(ws + w.q); a.xn = (_Float16*)(ws + w.xn); a.hid = (_Float16*)(ws + w.hid);
+    a.qbuf = (__bf16*)(ws + w.q); a.xn = xn; a.hid = (_Float16*)(ws + w.hid);
+    a.ss = ss; a.ss_parts = l == 0 ? 1 : s.d / 32;
+    a.next_ga = l + 1 < s.L ? (const float*)((const char*)packed + lo[l + 1].s_ga) : nullptr;
     rc = run_s_layer(s, (const char*)packed, lo[l], a, stream);
     if (rc) return rc;
   }
