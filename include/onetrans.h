@@ -182,7 +182,12 @@ int onetrans_score_candidates(const onetrans_config* cfg, const void* packed,
  * in the workspace, then scoring of each user's C candidates.
  *   s_tokens, s_lens, s_out as in onetrans_user_prefill
  *   ns_tokens dev bf16 [B][C][n_ns][d], ns_out dev fp32 [B][C][n_ns][d]
- * Size the workspace with onetrans_block_forward_workspace_bytes. */
+ * Size the workspace with onetrans_block_forward_workspace_bytes (the cache plus
+ * separate prefill and scoring areas). The S side runs on `stream`; the NS side
+ * runs concurrently on a second stream that the library creates on first use for
+ * the calling thread and device (default priority, kept until the process
+ * ends), and NS layer l waits only for the S side's layer-l cache rows. Work
+ * queued on `stream` after the call waits for both sides. */
 size_t onetrans_block_forward_workspace_bytes(const onetrans_config* cfg, int32_t B, int32_t C);
 int onetrans_block_forward(const onetrans_config* cfg, const void* packed,
                            const uint16_t* s_tokens, const int32_t* s_lens, int32_t B,

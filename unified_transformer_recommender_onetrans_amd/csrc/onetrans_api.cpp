@@ -224,6 +224,7 @@ struct SLayerArgs {
   __bf16* qbuf; _Float16* xn; _Float16* hid;
   float* ss; int ss_parts;   // the layer input's partial sums (deferred RMSNorm) and their count
   const float* next_ga;      // attention-norm gain of the next layer; NULL after the last
+  hipEvent_t kv_done;        // recorded once the layer's K/V rows are written; may be NULL
 };
 
 NormOut norm_out(const Shape& s, _Float16* xg, const float* gain, long gain_group_stride, float* ss) {
@@ -254,6 +255,7 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
     FamilyTimer t(ONETRANS_K_S_QKV, st);
     OT_HIP(launch_gemm(GEMM_QKV, false, false, g, st), "S QKV GEMM launch");
   }
+  if (a.kv_done) OT_HIP(hipEventRecord(a.kv_done, st), "layer event record");
 
   AttnParams at;
   memset(&at, 0, sizeof(at));
@@ -298,9 +300,11 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
   return ONETRANS_OK;
 }
 
+// kv_ready (may be NULL): per layer, an event after which that layer's cache K/V is
+// complete; the NS attention of the layer waits for it.
 int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const char* cache_buf, const size_t* k_off,
                const size_t* v_off, int n_users, int n_appended, int user, const uint16_t* ns_tokens, int C,
-               float* ns_out, char* ws, hipStream_t st) {
+               float* ns_out, char* ws, hipStream_t st, const hipEvent_t* kv_ready = nullptr) {
   if (C == 0) return ONETRANS_OK;
   const ScoreWs w = score_ws(s, C);
   __bf16* qn = (__bf16*)(ws + w.qn);
@@ -353,6 +357,7 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     at.kn = kn; at.vn = vn; at.kn_head_stride = rows * s.dh; at.P = s.P;
     at.scale_log2 = scale_log2(s);
     at.nout = norm_out(s, xn, (const float*)(pk + lo[l].ns_gf), d, ss);
+    if (kv_ready) OT_HIP(hipStreamWaitEvent(st, kv_ready[l], 0), "layer event wait");
     {
       FamilyTimer t(ONETRANS_K_NS_ATTN, st);
       OT_HIP(launch_attention(true, s.dh, at, 1, st), "NS attention launch");
@@ -388,9 +393,10 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
   return ONETRANS_OK;
 }
 
+// kv_done (may be NULL): per layer, an event recorded once that layer's cache K/V is written
 int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const uint16_t* s_tokens,
                  const int32_t* s_lens, int B, char* cache_buf, const size_t* k_off, const size_t* v_off,
-                 float* s_out, char* ws, hipStream_t st) {
+                 float* s_out, char* ws, hipStream_t st, const hipEvent_t* kv_done = nullptr) {
   const PrefillWs w = prefill_ws(s, B);
   float* x = (float*)(ws + w.x);
   float* ss = (float*)(ws + w.ss);
@@ -429,6 +435,7 @@ int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const u
     a.qbuf = (__bf16*)(ws + w.q); a.xn = xn; a.hid = (_Float16*)(ws + w.hid);
     a.ss = ss; a.ss_parts = l == 0 ? 1 : s.d / 32;
     a.next_ga = l + 1 < s.L ? (const float*)(pk + lo[l + 1].s_ga) : nullptr;
+    a.kv_done = kv_done ? kv_done[l] : nullptr;
     int rc = run_s_layer(s, pk, lo[l], a, st);
     if (rc) return rc;
   }
@@ -439,6 +446,33 @@ int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const u
                               (long)qL * s.d, B, st),
          "S output copy launch");
   }
+  return ONETRANS_OK;
+}
+
+// A second stream per thread and device for block_forward, with its fork / join and
+// per-layer events; created on first use (default priority) and kept until the process
+// ends. Thread-local, so calls from different threads stay independent.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t layer[ONETRANS_MAX_LAYERS] = {};
+};
+constexpr int kMaxDevices = 64;
+thread_local SideStream g_side[kMaxDevices];
+
+int side_stream(SideStream** out) {
+  int dev = 0;
+  OT_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ONETRANS_ERR_UNSUPPORTED, "device index out of range");
+  SideStream& ss = g_side[dev];
+  if (!ss.st) {
+    OT_HIP(hipStreamCreateWithFlags(&ss.st, hipStreamNonBlocking), "side stream create");
+    OT_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming), "event create");
+    OT_HIP(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming), "event create");
+    for (int l = 0; l < ONETRANS_MAX_LAYERS; ++l)
+      OT_HIP(hipEventCreateWithFlags(&ss.layer[l], hipEventDisableTiming), "event create");
+  }
+  *out = &ss;
   return ONETRANS_OK;
 }
 
@@ -555,10 +589,9 @@ size_t onetrans_workspace_bytes(const onetrans_config* cfg, int32_t max_users, i
 size_t onetrans_block_forward_workspace_bytes(const onetrans_config* cfg, int32_t B, int32_t C) {
   Shape s;
   if (make_shape(cfg, s) || B < 1 || C < 0) return 0;
-  size_t rest = prefill_ws(s, B).total;
-  const size_t c = score_ws(s, C).total;
-  if (c > rest) rest = c;
-  return cache_layout(s, B, nullptr, nullptr) + rest;
+  // the cache, then the prefill's and the scoring's workspaces side by side (they run
+  // concurrently)
+  return cache_layout(s, B, nullptr, nullptr) + prefill_ws(s, B).total + score_ws(s, C).total;
 }
 
 int onetrans_user_prefill(const onetrans_config* cfg, const void* packed, const uint16_t* s_tokens,
@@ -634,6 +667,7 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
     a.qbuf = (__bf16*)(ws + w.q); a.xn = xn; a.hid = (_Float16*)(ws + w.hid);
     a.ss = ss; a.ss_parts = l == 0 ? 1 : s.d / 32;
     a.next_ga = l + 1 < s.L ? (const float*)((const char*)packed + lo[l + 1].s_ga) : nullptr;
+    a.kv_done = nullptr;
     rc = run_s_layer(s, (const char*)packed, lo[l], a, stream);
     if (rc) return rc;
   }
@@ -687,15 +721,30 @@ int onetrans_block_forward(const onetrans_config* cfg, const void* packed, const
   size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
   const size_t cache_bytes = cache_layout(s, B, k_off, v_off);
   char* cb = (char*)workspace;
-  char* rest = cb + cache_bytes;
-  rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, cb, k_off, v_off, s_out, rest, stream);
+  char* pws = cb + cache_bytes;
+  char* sws = pws + prefill_ws(s, B).total;
+  if (C == 0)
+    return prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, cb, k_off, v_off, s_out, pws, stream);
+  // The S side runs on `stream`; the NS side on this thread's second stream, which starts
+  // after everything queued on `stream` so far and whose layer l waits only for the
+  // event after the S side's layer-l QKV (the cache rows it reads). The NS side's small
+  // dependence on the S side lets the latency-bound S layers fill idle CUs.
+  SideStream* side = nullptr;
+  rc = side_stream(&side);
+  if (rc) return rc;
+  OT_HIP(hipEventRecord(side->fork, stream), "fork event record");
+  OT_HIP(hipStreamWaitEvent(side->st, side->fork, 0), "fork event wait");
+  rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, cb, k_off, v_off, s_out, pws, stream,
+                    side->layer);
   if (rc) return rc;
   const long per_user = (long)C * s.P * s.d;
   for (int u = 0; u < B; ++u) {
     rc = score_impl(s, (const char*)packed, lo, cb, k_off, v_off, B, 0, u, ns_tokens + u * per_user, C,
-                    ns_out + u * per_user, rest, stream);
+                    ns_out + u * per_user, sws, side->st, side->layer);
     if (rc) return rc;
   }
+  OT_HIP(hipEventRecord(side->join, side->st), "join event record");
+  OT_HIP(hipStreamWaitEvent(stream, side->join, 0), "join event wait");
   return ONETRANS_OK;
 }
 
