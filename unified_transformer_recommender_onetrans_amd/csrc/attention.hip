@@ -90,20 +90,28 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&s
   st.l += ps;
 }
 
-// One 64-key tile against a wave's 32 queries: S^T = K Q^T, masking when a bound falls
-// inside the tile, the online-softmax update and O^T += V^T P^T. sb holds the tile: K rows
+// Pieces of one 64-key tile against a wave's 32 queries. sb holds the tile: K rows
 // (XOR-swizzled 16-byte chunks) followed by V^T rows of 64 keys (128 bytes each).
+//
+// Key order. The MFMA output puts S^T row 8*(j/4) + 4*(lane/32) + j%4 in register j. The
+// K operand's rows are taken with bits 2 and 3 of the row index swapped (within each
+// 16-key group, rows 4-7 and 8-11 trade places), so register j of block kb holds key
+//   kb*32 + 16*(j/8) + 8*(lane/32) + j%8,
+// and the 8 probabilities a lane packs for one P.V operand are 8 consecutive keys: the
+// matching V^T operand is a single 16-byte LDS read.
+__device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// S^T = K Q^T (raw scores)
 template <int DH>
-__device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, int my_lim, bool edge,
-                                          const bf16x8 (&qf)[DH / 16], Softmax<DH>& st, float scale) {
-  constexpr int KROW = DH * 2, K_BYTES = KT * KROW, KCH = KROW / 16;
-  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  f32x16 sc[2];
+__device__ __forceinline__ void qk_tile(const char* sb, const bf16x8 (&qf)[DH / 16], f32x16 (&sc)[2]) {
+  constexpr int KROW = DH * 2, KCH = KROW / 16;
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const int pl = key_perm(lane & 31);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) sc[kb][j] = 0.f;
-    const int r = kb * 32 + l32;
+    const int r = kb * 32 + pl;
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
       const int c = 2 * s + half;
@@ -112,32 +120,50 @@ __device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, in
       sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[kb], 0, 0, 0);
     }
   }
-  if (edge) {  // a mask boundary falls inside this tile
+}
+
+// keys of slots outside [key_lo, my_lim) get -inf (tile starting at slot t0)
+__device__ __forceinline__ void mask_tile(f32x16 (&sc)[2], int t0, int key_lo, int my_lim) {
+  const int half = (threadIdx.x >> 5) & 1;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int slot = t0 + kb * 32 + 8 * (j >> 2) + half * 4 + (j & 3);
-        if (slot < key_lo || slot >= my_lim) sc[kb][j] = -INFINITY;
-      }
-  }
-  bf16x8 pb[2][2];
-  softmax_update<DH, 2>(st, sc, pb, scale);
+    for (int j = 0; j < 16; ++j) {
+      const int slot = t0 + kb * 32 + 16 * (j >> 3) + 8 * half + (j & 7);
+      if (slot < key_lo || slot >= my_lim) sc[kb][j] = -INFINITY;
+    }
+}
+
+// O^T += V^T P^T with the tile's bf16 probabilities
+template <int DH>
+__device__ __forceinline__ void pv_tile(const char* sb, const bf16x8 (&pb)[2][2], Softmax<DH>& st) {
+  constexpr int KROW = DH * 2, K_BYTES = KT * KROW;
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db) {
-        // keys kb*32 + 16c + 4*half + {0..3} and + 8: chunk 4kb + 2c (+1), byte 8*half
+        // keys kb*32 + 16c + 8*half + 0..7: 16-byte chunk 4kb + 2c + half of V^T row r
         const int r = db * 32 + l32;
-        const int ch = 4 * kb + 2 * c;
-        const char* row = sb + K_BYTES + r * 128 + half * 8;
-        const bf16x4 lo = *(const bf16x4*)(row + ((ch ^ ((r >> 1) & 7)) << 4));
-        const bf16x4 hi = *(const bf16x4*)(row + (((ch + 1) ^ ((r >> 1) & 7)) << 4));
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int ch = 4 * kb + 2 * c + half;
+        const bf16x8 a = *(const bf16x8*)(sb + K_BYTES + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
         st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][c], st.o[db], 0, 0, 0);
       }
+}
+
+// One whole tile: scores, masking when a bound falls inside it, the online-softmax update
+// and the P.V product.
+template <int DH>
+__device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, int my_lim, bool edge,
+                                          const bf16x8 (&qf)[DH / 16], Softmax<DH>& st, float scale) {
+  f32x16 sc[2];
+  qk_tile<DH>(sb, qf, sc);
+  if (edge) mask_tile(sc, t0, key_lo, my_lim);
+  bf16x8 pb[2][2];
+  softmax_update<DH, 2>(st, sc, pb, scale);
+  pv_tile<DH>(sb, pb, st);
 }
 
 // Output of query row qi, in two parts. out_row_load fetches this lane's half of head h's
