@@ -51,12 +51,14 @@ struct Softmax {
   f32x16 o[DH / 32];
 };
 
-// Online-softmax update with NB 32-key blocks of raw scores (masked entries -inf).
+// Online-softmax update with NB 32-key blocks of raw scores (masked entries -inf). With
+// SUM false the caller adds the probabilities' sum to l itself (attn_tile does it on the
+// matrix core).
 // The scale 1/sqrt(dh) * log2(e) is applied inside exp2 as one fma. The O
 // accumulators are rescaled only when some lane's running max grew: otherwise
 // the factor is exactly 1 and the multiply is skipped. Returns the bf16
 // probabilities packed as the B operands of the P.V product.
-template <int DH, int NB>
+template <int DH, int NB, bool SUM = true>
 __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&sc)[NB], bf16x8 (&pb)[NB][2],
                                                float scale) {
   float mt = -INFINITY;
@@ -84,10 +86,10 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&s
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(sc[b][8 * c + i], scale, msub));
-        ps += pv;
+        if (SUM) ps += pv;
         pb[b][c][i] = (__bf16)pv;
       }
-  st.l += ps;
+  if (SUM) st.l += ps;
 }
 
 // Pieces of one 64-key tile against a wave's 32 queries. sb holds the tile: K rows
@@ -162,8 +164,20 @@ __device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, in
   qk_tile<DH>(sb, qf, sc);
   if (edge) mask_tile(sc, t0, key_lo, my_lim);
   bf16x8 pb[2][2];
-  softmax_update<DH, 2>(st, sc, pb, scale);
+  softmax_update<DH, 2, false>(st, sc, pb, scale);
   pv_tile<DH>(sb, pb, st);
+  // the tile's probability sum on the matrix core: an all-ones A operand turns every
+  // output row of 1 P^T into the column sums (the same bf16 P that multiplies V). Both
+  // half-waves get the full sum (bit-identical rows) while l is kept as per-half partial
+  // sums that are added at the end, so each half adds half of it (exact in fp32).
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  f32x16 ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0][0], f32x16{}, 0, 0, 0);
+  ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0][1], ls, 0, 0, 0);
+  ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[1][0], ls, 0, 0, 0);
+  ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[1][1], ls, 0, 0, 0);
+  st.l += 0.5f * ls[0];
 }
 
 // Output of query row qi, in two parts. out_row_load fetches this lane's half of head h's
@@ -253,7 +267,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   constexpr int KRPI = 64 / KCH;              // K rows per wave instruction
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: kept in a scalar register, so per-wave LDS addresses are too
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y, seg = blockIdx.z;
   const int wq0 = blockIdx.x * (NW * 32) + wave * 32;
@@ -302,18 +317,18 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   // ---- per-lane sources of the tile DMA (slots beyond the filled length hold zeros) ----
   const char* kbase = (const char*)(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride);
   const char* vbase = (const char*)(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride);
-  long k_off[K_INSTR], v_off[V_INSTR];
+  uint32_t k_off[K_INSTR], v_off[V_INSTR];  // per-lane byte offsets from the uniform tile base
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
     const int r = (wave * K_INSTR + i) * KRPI + lane / KCH;
     const int c = lane % KCH;
     const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
-    k_off[i] = (long)r * KROW + cs * 16;
+    k_off[i] = (uint32_t)(r * KROW + cs * 16);
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
     const int r = (wave * V_INSTR + i) * 8 + (lane >> 3);   // dh row
-    v_off[i] = (long)r * p.kv_cap * 2 + ((((lane & 7) ^ ((r >> 1) & 7))) << 4);
+    v_off[i] = (uint32_t)r * (uint32_t)p.kv_cap * 2u + ((((lane & 7) ^ ((r >> 1) & 7))) << 4);
   }
   auto issue = [&](int t0, int stage) {
     char* sb = smem + stage * STAGE;
@@ -394,6 +409,217 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   const float l_tot = st.l + __shfl_xor(st.l, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) out_row_store<DH, EARLY_G>(p, seg, h, qi, orow, st.o, inv);
+}
+
+// NS queries with every 64-key tile split between two waves: wave pair (2b, 2b + 1) holds
+// query block b, and wave 2b + kh scores keys kh*32 .. kh*32 + 31 of each tile. Every NS
+// lane sees the same cached-key range [key_lo, n_keys), so all waves walk the same tiles
+// of one shared stream; splitting the keys doubles the waves per SIMD, which hides the
+// latencies of the per-tile chain (LDS read, MFMA, max exchange, exponentials, P.V).
+// After the last tile the halves' (max, sum, O) merge through LDS; the key-half-0 wave
+// adds the candidate's own NS keys first and writes the result.
+template <int DH, int NB>
+__global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
+  constexpr int NW = 2 * NB;                  // waves per workgroup
+  constexpr int KROW = DH * 2;
+  constexpr int K_BYTES = KT * KROW;
+  constexpr int V_BYTES = DH * KT * 2;
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int K_INSTR = K_BYTES / 1024 / NW;  // DMA instructions per wave and tile
+  constexpr int V_INSTR = V_BYTES / 1024 / NW;
+  static_assert(K_INSTR >= 1 && V_INSTR >= 1 && K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0, "tile split");
+  constexpr int PER_TILE = K_INSTR + V_INSTR;
+  constexpr int KCH = KROW / 16;
+  constexpr int KRPI = 64 / KCH;
+  constexpr int MERGE = 64 * (2 + 16 * (DH / 32)) * 4;  // one wave's m, l and O for 64 lanes
+  static_assert(NB * MERGE <= STAGES * STAGE, "merge area");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int qb = wave >> 1, kh = wave & 1;
+  const int h = blockIdx.y;
+  const int wq0 = blockIdx.x * (NB * 32) + qb * 32;
+  const int qi = wq0 + l32;
+  const bool q_ok = qi < p.nq;
+  const bool wave_live = wq0 < p.nq;
+
+  bf16x8 qf[DH / 16];
+  {
+    const __bf16* qrow = p.q + h * p.q_head_stride + (long)(q_ok ? qi : 0) * DH;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+      bf16x8 v = *(const bf16x8*)(qrow + s * 16 + half * 8);
+      if (!q_ok) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.f;
+      }
+      qf[s] = v;
+    }
+  }
+  const int key_lo = max(0, p.valid_from[0] - p.key_pos0);
+  const int n_keys = p.n_keys;
+  const int my_lim = q_ok ? n_keys : 0;
+  const int full_lim = wq0 + 31 < p.nq ? n_keys : 0;  // tiles ending at or below it need no mask
+
+  Softmax<DH> st;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st.o[db][j] = 0.f;
+
+  // ---- per-lane sources of the tile DMA (slots beyond the filled length hold zeros) ----
+  const char* kbase = (const char*)(p.k + h * p.kv_head_stride);
+  const char* vbase = (const char*)(p.vt + h * p.kv_head_stride);
+  uint32_t k_off[K_INSTR], v_off[V_INSTR];
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) {
+    const int r = (wave * K_INSTR + i) * KRPI + lane / KCH;
+    const int c = lane % KCH;
+    const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+    k_off[i] = (uint32_t)(r * KROW + cs * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < V_INSTR; ++i) {
+    const int r = (wave * V_INSTR + i) * 8 + (lane >> 3);   // dh row
+    v_off[i] = (uint32_t)r * (uint32_t)p.kv_cap * 2u + ((((lane & 7) ^ ((r >> 1) & 7))) << 4);
+  }
+  auto issue = [&](int t0, int stage) {
+    char* sb = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < K_INSTR; ++i)
+      dma16(kbase + (long)t0 * KROW + k_off[i], (lds_void*)(sb + (wave * K_INSTR + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < V_INSTR; ++i)
+      dma16(vbase + (long)t0 * 2 + v_off[i], (lds_void*)(sb + K_BYTES + (wave * V_INSTR + i) * 1024));
+  };
+
+  const int t_first = (key_lo / KT) * KT;
+  const int ntiles = n_keys > t_first ? (n_keys - t_first + KT - 1) / KT : 0;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < ntiles) issue(t_first + s * KT, s);
+
+  const int pl = key_perm(l32);  // score row order: see qk_tile
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+#pragma unroll 1
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) wait_vmcnt<PER_TILE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (it + STAGES - 1 < ntiles) issue(t_first + (it + STAGES - 1) * KT, (it + STAGES - 1) % STAGES);
+    const int t0 = t_first + it * KT;
+    const char* sb = smem + (it % STAGES) * STAGE;
+    // this wave's 32 keys of the tile
+    f32x16 sc[1];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sc[0][j] = 0.f;
+    {
+      const int r = kh * 32 + pl;
+#pragma unroll
+      for (int s = 0; s < DH / 16; ++s) {
+        const int c = 2 * s + half;
+        const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+        const bf16x8 a = *(const bf16x8*)(sb + r * KROW + cs * 16);
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[0], 0, 0, 0);
+      }
+    }
+    if (t0 < key_lo || t0 + KT > full_lim) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int slot = t0 + kh * 32 + 16 * (j >> 3) + 8 * half + (j & 7);
+        if (slot < key_lo || slot >= my_lim) sc[0][j] = -INFINITY;
+      }
+    }
+    bf16x8 pb[1][2];
+    softmax_update<DH, 1, false>(st, sc, pb, p.scale_log2);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) {
+        const int r = db * 32 + l32;
+        const int ch = 4 * kh + 2 * c + half;
+        const bf16x8 a = *(const bf16x8*)(sb + K_BYTES + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][c], st.o[db], 0, 0, 0);
+      }
+    // the probability sum on the matrix core (see attn_tile)
+    f32x16 ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0][0], f32x16{}, 0, 0, 0);
+    ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0][1], ls, 0, 0, 0);
+    st.l += 0.5f * ls[0];
+  }
+
+  if (kh == 0 && wave_live) {
+    // the candidate's own NS keys: query g = c*P + k sees g' in [c*P, g];
+    // NS K and V are row-major [H][nq][dh]
+    const int P = p.P;
+    const int g_lo = (wq0 / P) * P;
+    const int g_hi = min(wq0 + 31, p.nq - 1);
+    const int my_first = (qi / P) * P;
+    const __bf16* knb = p.kn + h * p.kn_head_stride;
+    const __bf16* vnb = p.vn + h * p.kn_head_stride;
+#pragma unroll 1
+    for (int t0 = g_lo; t0 <= g_hi; t0 += 32) {
+      f32x16 sk[1];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sk[0][j] = 0.f;
+      const int krow = min(t0 + l32, p.nq - 1);
+#pragma unroll
+      for (int s = 0; s < DH / 16; ++s) {
+        const bf16x8 a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
+        sk[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sk[0], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = t0 + 8 * (j >> 2) + half * 4 + (j & 3);
+        const bool vis = q_ok && key <= qi && key >= my_first;
+        if (!vis) sk[0][j] = -INFINITY;
+      }
+      bf16x8 pk[1][2];
+      softmax_update<DH, 1>(st, sk, pk, p.scale_log2);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < DH / 32; ++db) {
+          bf16x8 a;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), p.nq - 1);
+            a[i] = vnb[(long)key * DH + db * 32 + l32];
+          }
+          st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][c], st.o[db], 0, 0, 0);
+        }
+    }
+  }
+
+  // ---- merge the two key halves of each query block (LDS of the tile ring is free) ----
+  const float l_half = st.l + __shfl_xor(st.l, 32);
+  __syncthreads();  // every wave is past its last tile read
+  float* mw = (float*)(smem + qb * MERGE);
+  if (kh == 1) {
+    mw[lane] = st.m;
+    mw[64 + lane] = l_half;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mw[128 + (db * 16 + j) * 64 + lane] = st.o[db][j];
+  }
+  __syncthreads();
+  if (kh == 1 || !q_ok) return;
+  OutRow<DH> orow;
+  out_row_load<DH, true>(p, 0, h, qi, orow);
+  const float m1 = mw[lane], l1 = mw[64 + lane];
+  const float m = fmaxf(st.m, m1);
+  const float f0 = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - m) * p.scale_log2);
+  const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * p.scale_log2);
+  const float l_tot = l_half * f0 + l1 * f1;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st.o[db][j] = st.o[db][j] * f0 + mw[128 + (db * 16 + j) * 64 + lane] * f1;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  out_row_store<DH, true>(p, 0, h, qi, orow, st.o, inv);
 }
 
 // S-token attention with the keys of one 32-query block split over KS waves: wave w takes
@@ -538,6 +764,12 @@ __global__ void cache_clear_tail_kernel(ClearTailParams p) {
 
 }  // namespace
 
+template <int DH, int NB>
+void launch_attn_ns2(const AttnParams& p, hipStream_t s) {
+  dim3 grid((p.nq + NB * 32 - 1) / (NB * 32), p.H, 1);
+  hipLaunchKernelGGL((attn_ns2_kernel<DH, NB>), grid, dim3(NB * 128), 0, s, p);
+}
+
 template <int NW>
 void launch_attn_nw(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s) {
   dim3 grid((p.nq + NW * 32 - 1) / (NW * 32), p.H, n_seg);
@@ -558,7 +790,18 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
   // when the grid would leave CUs idle (one user's prefill has few query blocks per head);
   // the K/V of a layer is L2-resident, so streaming it to more workgroups is cheap.
   const long blocks32 = (long)((p.nq + 31) / 32) * p.H * n_seg;
-  if (!ns && blocks32 < 2L * 512) {
+  if (ns) {
+    // NS: each tile's keys split over two waves per query block; 2 query blocks (4 waves)
+    // per workgroup when there are blocks for 512 such workgroups, else 1
+    if (n_seg != 1) return hipErrorInvalidValue;
+    if (dh == 64) {
+      if (blocks32 >= 2L * 512) launch_attn_ns2<64, 2>(p, s);
+      else launch_attn_ns2<64, 1>(p, s);
+    } else {
+      if (blocks32 >= 2L * 512) launch_attn_ns2<32, 2>(p, s);
+      else launch_attn_ns2<32, 1>(p, s);
+    }
+  } else if (blocks32 < 2L * 512) {
     // few S query blocks: split each block's keys over four waves
     dim3 grid((p.nq + 31) / 32, p.H, n_seg);
     if (dh == 64) hipLaunchKernelGGL((attn_split_kernel<64, 4>), grid, dim3(256), 0, s, p);
