@@ -257,28 +257,47 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
       const int s = t * nk + kt;
       lds_barrier();  // step s is in LDS
       const char* st = smem + (s % STAGES) * STAGE;
+      // Fragments of a group of 16-wide k-steps are all read before its MFMAs: with one
+      // register set per k-step the reads of step ks + 1 could only start after step ks's
+      // MFMAs had consumed the registers, exposing the LDS latency at every k-step.
+      constexpr int KS = BK / 16;
+      constexpr int FG = MI + NI <= 4 ? KS : KS / 2;  // k-steps per group (register budget)
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        f16x8 a[MI], b[NI];
-        const int c = 2 * ks + (lane >> 5);
+      for (int g0 = 0; g0 < KS; g0 += FG) {
+        f16x8 a[FG][MI];
+        f16x8 b[FG][NI];
+        uint2 b8[FG][NI];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          const int r = wm * TM + mi * 32 + (lane & 31);
-          a[mi] = *(const f16x8*)(st + r * AROW + (swz<AROW>(c, r) << 4));
+        for (int kk = 0; kk < FG; ++kk) {
+          const int ks = g0 + kk;
+          const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) {
+            const int r = wm * TM + mi * 32 + (lane & 31);
+            a[kk][mi] = *(const f16x8*)(st + r * AROW + (swz<AROW>(c, r) << 4));
+          }
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const int r = wn * TN + ni * 32 + (lane & 31);
+            if (FP8)
+              b8[kk][ni] = *(const uint2*)(st + A_BYTES + r * 64 + (swz<64>(ks, r) << 4) + (lane >> 5) * 8);
+            else
+              b[kk][ni] = *(const f16x8*)(st + A_BYTES + r * BROW + (swz<BROW>(c, r) << 4));
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep every read of the group ahead of its MFMAs
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int r = wn * TN + ni * 32 + (lane & 31);
-          if (FP8)
-            b[ni] = e4m3x8_to_f16(*(const uint2*)(st + A_BYTES + r * 64 + (swz<64>(ks, r) << 4) + (lane >> 5) * 8));
-          else
-            b[ni] = *(const f16x8*)(st + A_BYTES + r * BROW + (swz<BROW>(c, r) << 4));
+        for (int kk = 0; kk < FG; ++kk) {
+          if (FP8) {
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) b[kk][ni] = e4m3x8_to_f16(b8[kk][ni]);
+          }
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[kk][ni], a[kk][mi], acc[mi][ni], 0, 0, 0);
         }
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[ni], a[mi], acc[mi][ni], 0, 0, 0);
       }
     }
 
@@ -447,7 +466,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
   }
 }
 
-// Tile shapes: (BM, BN, compute waves along M). The operand ring takes up to 159 KB of
+// Tile shapes: (BM, BN, compute waves along M). 96-wide tiles are fp16-only (a 96-row E4M3
+// tile is not a whole number of 4 KB DMA rounds). The operand ring takes up to 159 KB of
 // LDS, at most 8 stages.
 template <int KD, int BM, int BN, int WM, bool FP8>
 constexpr int stages_for() {
@@ -492,10 +512,10 @@ void launch_kind(bool fp8, const GemmParams& p, hipStream_t s) {
   // a Q / K / V tile must not straddle two of them: BN divides d
   auto fits = [&](int bn) { return p.N % bn == 0 && (KD != GEMM_QKV || p.d % bn == 0) && !(fp8 && bn == 96); };
   // ties go to the earlier entry: the smaller tile, which leaves fewer CUs idle in the last round
-  const TileCfg cands[5] = {{128, 96}, {128, 128}, {256, 128}, {128, 64}, {64, 64}};
+  const TileCfg cands[6] = {{128, 96}, {128, 128}, {256, 96}, {256, 128}, {128, 64}, {64, 64}};
   int best = -1;
   double best_cost = 0;
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < 6; ++i) {
     if (!fits(cands[i].bn)) continue;
     const double c = tile_cost(p, fp8, cands[i].bm, cands[i].bn);
     if (best < 0 || c < best_cost) { best = i; best_cost = c; }
@@ -503,8 +523,9 @@ void launch_kind(bool fp8, const GemmParams& p, hipStream_t s) {
   switch (best) {
     case 0: launch_cfg<KD, SIDE, 128, 96, 4>(fp8, p, s); break;
     case 1: launch_cfg<KD, SIDE, 128, 128, 2>(fp8, p, s); break;
-    case 2: launch_cfg<KD, SIDE, 256, 128, 2>(fp8, p, s); break;
-    case 3: launch_cfg<KD, SIDE, 128, 64, 2>(fp8, p, s); break;
+    case 2: launch_cfg<KD, SIDE, 256, 96, 4>(fp8, p, s); break;
+    case 3: launch_cfg<KD, SIDE, 256, 128, 2>(fp8, p, s); break;
+    case 4: launch_cfg<KD, SIDE, 128, 64, 2>(fp8, p, s); break;
     default: launch_cfg<KD, SIDE, 64, 64, 2>(fp8, p, s); break;
   }
 }
