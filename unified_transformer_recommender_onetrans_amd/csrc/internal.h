@@ -8,23 +8,26 @@ namespace onetrans {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// GELU(x) = x/2 (1 + erf(x / sqrt 2)) with erf from Abramowitz & Stegun,
-// Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 for all
-// x): erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0.
-// About 14 VALU operations; its error is three orders of magnitude below the
-// fp16 rounding applied to the result.
+// GELU(x) = x Phi(x), Phi the standard normal CDF, with erfc from Abramowitz & Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26 (|error of erf| <= 1.5e-7 for all x):
+// erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0. Written as
+//   GELU(x) = max(x, 0) - |x| Phi(-|x|),  Phi(-|x|) = erfc(|x| / sqrt 2) / 2,
+// which holds for both signs, with 1/2 folded into the coefficients and 1/sqrt 2 into p:
+// 12 VALU operations plus one reciprocal and one exp2. The approximation error is three
+// orders of magnitude below the fp16 rounding applied to the result.
 __device__ __forceinline__ float gelu_as(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float q = fmaf(1.061405429f, t, -1.453152027f);
-  q = fmaf(q, t, 1.421413741f);
-  q = fmaf(q, t, -0.284496736f);
-  q = fmaf(q, t, 0.254829592f);
-  q *= t;
-  const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
-  const float erf_abs = fmaf(-q, e, 1.0f);
-  const float hx = 0.5f * x;
-  return fmaf(hx, __builtin_copysignf(erf_abs, x), hx);
+  constexpr float kP = 0.3275911f * 0.70710678118654752f;
+  constexpr float kA1 = 0.5f * 0.254829592f, kA2 = 0.5f * -0.284496736f, kA3 = 0.5f * 1.421413741f,
+                  kA4 = 0.5f * -1.453152027f, kA5 = 0.5f * 1.061405429f;
+  constexpr float kE = -0.5f * 1.4426950408889634f;  // exp(-x^2 / 2) = exp2(kE x^2)
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(kP, a, 1.0f));
+  float q = fmaf(kA5, t, kA4);
+  q = fmaf(q, t, kA3);
+  q = fmaf(q, t, kA2);
+  q = fmaf(q, t, kA1);
+  const float e = __builtin_amdgcn_exp2f((x * x) * kE);
+  return fmaf(-(a * (q * t)), e, fmaxf(x, 0.0f));
 }
 
 // The value that lane l ^ 32 holds (v_permlane32_swap: no LDS traffic). Both lanes of a
