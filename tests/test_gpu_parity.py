@@ -11,7 +11,7 @@ import pytest
 import oracle as O
 from onetrans_inputs import (CANDIDATE_HEAVY_FP8, ONETRANS_L, ONETRANS_S, PREFILL_BATCH, TINY, Workload,
                              make_append_tokens, make_ns_tokens, make_s_tokens)
-from helpers import EPS, assert_close, bf16_dev, model
+from helpers import EPS, assert_close, bf16_dev, config, device_weights, model, weights
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -96,6 +96,46 @@ def test_prefill_append_score_match_oracle(name):
             ok = (oc.base[l] + np.arange(rows)) >= oc.valid_from
             assert_close(k.float().cpu().numpy()[ok], oc.k[l][ok], "bf16", f"user {u} layer {l} cached K")
             assert_close(v.float().cpu().numpy()[ok], oc.v[l][ok], "bf16", f"user {u} layer {l} cached V")
+
+
+def test_peaked_attention_moves_softmax_reference():
+    """Cached keys far above the first key tile's scores: the NS kernel's online softmax
+    has to move its reference maximum in the middle of the key stream (its rescale
+    path) and must still match the oracle."""
+    from unified_transformer_recommender_onetrans_amd import OneTrans
+    wl = Workload(name="peak", n_layers=2, d_model=128, n_heads=2, ffn_hidden=256, s_len=300,
+                  q_sched=(300, 64), n_ns=32, n_users=1, n_candidates=3)
+    raw, _ = weights(wl)
+    raw = [dict(lw) for lw in raw]
+    d = wl.d_model
+    eye = np.eye(d, dtype=np.float32)
+    for lw in raw:  # W_Q = 1.5 I (NS) / I (S) and W_K = I, so scores are scaled dot products
+        sq = lw["s_wqkv"].copy()
+        sq[:d], sq[d:2 * d] = eye, eye
+        nq = lw["ns_wqkv"].copy()
+        nq[:, :d], nq[:, d:2 * d] = 1.5 * eye, eye
+        lw["s_wqkv"], lw["ns_wqkv"] = sq, nq
+    lay = O.layers_from_arrays(raw)
+    s, lens, ns = _inputs(wl, [300])
+    s[0, 128:] = ns[0, 0, 0]  # later events repeat candidate 0's first NS token
+    # the premise, from the oracle's layer-0 quantities: for NS query (candidate 0, row 0)
+    # the best cached key beats the best key of the first 64-key tile by more than 8 in
+    # log2 units in every head
+    W = lay[0]
+    q0 = O.rmsnorm(np.asarray(ns[0, 0, 0], np.float64), W.ns_ga[0], EPS) @ W.ns_wq[0].T
+    kS = O.rmsnorm(np.asarray(s[0], np.float64), W.s_ga, EPS) @ W.s_wk.T
+    dh = d // wl.n_heads
+    for h in range(wl.n_heads):
+        sl = slice(h * dh, (h + 1) * dh)
+        logits = kS[:, sl] @ q0[sl] / np.sqrt(dh)
+        assert (logits.max() - logits[:64].max()) * np.log2(np.e) > 8.5
+    m = OneTrans(config(wl), device_weights(raw))
+    s_out, ns_out = m.block_forward(*_dev(s, lens, ns))
+    torch.cuda.synchronize()
+    ref_t, ref_n = O.block_forward(lay, wl.q_sched, wl.n_heads, EPS, s, lens, ns)
+    assert_close(s_out.cpu().numpy(), ref_t, wl.ns_wdtype, "S tail")
+    assert_close(ns_out.cpu().numpy(), ref_n, wl.ns_wdtype, "NS out")
+    assert_close(ns_out[0, 0, 0].cpu().numpy(), ref_n[0, 0, 0], wl.ns_wdtype, "NS row of the peaked query")
 
 
 def test_zero_candidates_and_capacity_errors():

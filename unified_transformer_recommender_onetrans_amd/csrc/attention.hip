@@ -19,6 +19,8 @@
 // fragment reads are bank-conflict free. The result is added to the fp32
 // residual rows (z = x + o) without rounding.
 #include <math.h>
+
+#include <type_traits>
 #include "internal.h"
 
 namespace onetrans {
@@ -417,7 +419,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
 // of one shared stream; splitting the keys doubles the waves per SIMD, which hides the
 // latencies of the per-tile chain (LDS read, MFMA, max exchange, exponentials, P.V).
 // After the last tile the halves' (max, sum, O) merge through LDS; the key-half-0 wave
-// adds the candidate's own NS keys first and writes the result.
+// adds the candidate's own NS keys first and writes the result. Each tile's scores are
+// issued to the matrix core one iteration ahead, so the exponentials of a tile run while
+// the next tile's S^T is being computed.
 template <int DH, int NB>
 __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   constexpr int NW = 2 * NB;                  // waves per workgroup
@@ -484,71 +488,146 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     const int r = (wave * V_INSTR + i) * 8 + (lane >> 3);   // dh row
     v_off[i] = (uint32_t)r * (uint32_t)p.kv_cap * 2u + ((((lane & 7) ^ ((r >> 1) & 7))) << 4);
   }
-  auto issue = [&](int t0, int stage) {
-    char* sb = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < K_INSTR; ++i)
-      dma16(kbase + (long)t0 * KROW + k_off[i], (lds_void*)(sb + (wave * K_INSTR + i) * 1024));
-#pragma unroll
-    for (int i = 0; i < V_INSTR; ++i)
-      dma16(vbase + (long)t0 * 2 + v_off[i], (lds_void*)(sb + K_BYTES + (wave * V_INSTR + i) * 1024));
-  };
-
   const int t_first = (key_lo / KT) * KT;
   const int ntiles = n_keys > t_first ? (n_keys - t_first + KT - 1) / KT : 0;
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ntiles) issue(t_first + s * KT, s);
 
+  // K and V^T of a tile travel in rings of their own: iteration it reads K of tile it + 1
+  // (whose scores go to the matrix core first, so that tile it's softmax runs under them)
+  // and V^T of tile it. Issue order: K(0); K(1), V(0); K(2), V(1); then iteration it
+  // issues K(it + 3) and V(it + 2) into the slots that iteration it - 1 finished reading.
+  // Tile j lives in slot j % 3 of both rings; the loop is unrolled three times so that
+  // every slot offset is a compile-time constant.
+  static_assert(STAGES == 3, "ring of three slots");
+  char* const kring = smem;
+  char* const vring = smem + STAGES * K_BYTES;
+  auto issue_k = [&](int j, int slot) {
+    char* sb = kring + slot * K_BYTES;
+#pragma unroll
+    for (int i = 0; i < K_INSTR; ++i)
+      dma16(kbase + (long)(t_first + j * KT) * KROW + k_off[i], (lds_void*)(sb + (wave * K_INSTR + i) * 1024));
+  };
+  auto issue_v = [&](int j, int slot) {
+    char* sb = vring + slot * V_BYTES;
+#pragma unroll
+    for (int i = 0; i < V_INSTR; ++i)
+      dma16(vbase + (long)(t_first + j * KT) * 2 + v_off[i], (lds_void*)(sb + (wave * V_INSTR + i) * 1024));
+  };
+  // per-lane parts of the fragment addresses (the slot adds a constant)
   const int pl = key_perm(l32);  // score row order: see qk_tile
-  bf16x8 ones;
+  uint32_t k_frag[DH / 16], v_frag[2][DH / 32];
+  {
+    const int r = kh * 32 + pl;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
-#pragma unroll 1
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) wait_vmcnt<PER_TILE>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (it + STAGES - 1 < ntiles) issue(t_first + (it + STAGES - 1) * KT, (it + STAGES - 1) % STAGES);
-    const int t0 = t_first + it * KT;
-    const char* sb = smem + (it % STAGES) * STAGE;
-    // this wave's 32 keys of the tile
-    f32x16 sc[1];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) sc[0][j] = 0.f;
-    {
-      const int r = kh * 32 + pl;
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s) {
-        const int c = 2 * s + half;
-        const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
-        const bf16x8 a = *(const bf16x8*)(sb + r * KROW + cs * 16);
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[0], 0, 0, 0);
-      }
+    for (int s = 0; s < DH / 16; ++s) {
+      const int c = 2 * s + half;
+      const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+      k_frag[s] = (uint32_t)(r * KROW + cs * 16);
     }
-    if (t0 < key_lo || t0 + KT > full_lim) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int slot = t0 + kh * 32 + 16 * (j >> 3) + 8 * half + (j & 7);
-        if (slot < key_lo || slot >= my_lim) sc[0][j] = -INFINITY;
-      }
-    }
-    bf16x8 pb[1][2];
-    softmax_update<DH, 1, false>(st, sc, pb, p.scale_log2);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db) {
-        const int r = db * 32 + l32;
+        const int rv = db * 32 + l32;
         const int ch = 4 * kh + 2 * c + half;
-        const bf16x8 a = *(const bf16x8*)(sb + K_BYTES + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][c], st.o[db], 0, 0, 0);
+        v_frag[c][db] = (uint32_t)(rv * 128 + ((ch ^ ((rv >> 1) & 7)) << 4));
       }
-    // the probability sum on the matrix core (see attn_tile)
-    f32x16 ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0][0], f32x16{}, 0, 0, 0);
-    ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0][1], ls, 0, 0, 0);
-    st.l += 0.5f * ls[0];
   }
+  // raw scores S^T of this wave's 32 keys of the tile in K slot `slot`
+  auto scores = [&](int slot, f32x16& sc) {
+    const char* sb = kring + slot * K_BYTES;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sb + k_frag[s]), qf[s], sc, 0, 0, 0);
+  };
+  if (ntiles > 0) issue_k(0, 0);
+  if (ntiles > 1) issue_k(1, 1);
+  if (ntiles > 0) issue_v(0, 0);
+  if (ntiles > 2) issue_k(2, 2);
+  if (ntiles > 1) issue_v(1, 1);
+
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+  // Lazy rescaling: the reference max st.m only moves when a tile's max exceeds it by more
+  // than 8 in log2 units (probabilities then stay below 2^8, far inside fp32 and bf16 range;
+  // any reference gives the same normalised result), which on typical scores leaves the
+  // rescale of O to the first tile.
+  const float scale = p.scale_log2;
+  const float tau = 8.f / scale;
+  f32x16 sc;
+  if (ntiles > 0) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    scores(0, sc);
+  }
+  // iteration it with tile it in slot S0 (= it % 3)
+  auto step = [&](auto S0C, int it) {
+    constexpr int S0 = decltype(S0C)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+    if (it + 2 < ntiles) wait_vmcnt<PER_TILE>();  // K(it + 1) and V(it) are in
+    else if (it + 1 < ntiles) wait_vmcnt<V_INSTR>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (it + 3 < ntiles) issue_k(it + 3, S0);
+    if (it + 2 < ntiles) issue_v(it + 2, S2);
+    // next tile's scores first (after the last tile this reads a slot nobody writes any
+    // more; the result is unused)
+    f32x16 sn;
+    scores(S1, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    const int t0 = t_first + it * KT;
+    if (t0 < key_lo || t0 + KT > full_lim) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int slot = t0 + kh * 32 + 16 * (j >> 3) + 8 * half + (j & 7);
+        if (slot < key_lo || slot >= my_lim) sc[j] = -INFINITY;
+      }
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sc[j]);
+    mt = fmaxf(mt, other_half(mt));
+    if (__builtin_amdgcn_ballot_w64(mt > st.m + tau) != 0) {
+      const bool up = mt > st.m + tau;
+      const float alpha = up ? __builtin_amdgcn_exp2f((st.m - mt) * scale) : 1.f;
+      if (up) st.m = mt;
+      st.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st.o[db][j] *= alpha;
+    }
+    const float msub = st.m == -INFINITY ? 0.f : -st.m * scale;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[8 * c + i], scale, msub));
+    const char* vb = vring + S0 * V_BYTES;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + v_frag[c][db]), pb[c], st.o[db], 0, 0, 0);
+    // this half's sum of the same bf16 probabilities that multiply V
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 pr = {pb[c][2 * i], pb[c][2 * i + 1]};
+        st.l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, st.l, false);
+      }
+    sc = sn;
+  };
+  int it = 0;
+#pragma unroll 1
+  for (; it + 3 <= ntiles; it += 3) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
+    step(std::integral_constant<int, 2>{}, it + 2);
+  }
+  if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
+  if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
 
   if (kh == 0 && wave_live) {
     // the candidate's own NS keys: query g = c*P + k sees g' in [c*P, g];
