@@ -18,7 +18,11 @@ paragraphs; the asterzephyr.xyz blog, designs two to four, corroborates):
   output); keys and values cover every S-row that is input to the layer.
 * Cross-request KV sharing: because S precedes NS, the S-side K/V of every layer
   is computed once per user and reused for every candidate; appended events
-  extend it.
+  extend it. The user side also covers the profile fields (asterzephyr.xyz,
+  design four): when the first P_u NS positions hold user fields, they depend
+  on the user only, so they are computed once per user as well, their K/V is
+  cached beside the S-side K/V, and the candidate rows (positions P_u..P-1) see
+  them like any earlier NS row.
 
 Readings where the pages are silent (each is listed in the design notes):
   no biases, no output projection (heads are concatenated and added to the
@@ -223,23 +227,36 @@ def forward_dense(layers: Sequence[Layer], q_sched: Sequence[int], n_heads: int,
 
 @dataclass
 class UserCache:
-    """S-side K/V of one user, per layer.
+    """User-side K/V of one user, per layer.
 
     Row r of layer l holds global position base[l] + r; rows at global
-    positions < valid_from are padding and are never keys.
+    positions < valid_from are padding and are never keys. With user-side NS
+    fields, ns_tokens holds their inputs [P_u, d], nk / nv their K/V per layer
+    [P_u, d] and ns_out their outputs after the last layer.
     """
     base: List[int]
     valid_from: int
     k: List[np.ndarray] = field(default_factory=list)
     v: List[np.ndarray] = field(default_factory=list)
+    ns_tokens: Optional[np.ndarray] = None
+    nk: List[np.ndarray] = field(default_factory=list)
+    nv: List[np.ndarray] = field(default_factory=list)
+    ns_out: Optional[np.ndarray] = None
 
     def length(self, l: int) -> int:
         return self.k[l].shape[0]
 
+    @property
+    def n_user_ns(self) -> int:
+        return 0 if self.ns_tokens is None else self.ns_tokens.shape[0]
+
 
 def prefill(layers: Sequence[Layer], q_sched: Sequence[int], n_heads: int, eps: float,
-            s_tokens: np.ndarray, s_valid: int) -> Tuple[UserCache, np.ndarray]:
-    """S side of one user: per-layer K/V for every present row, queries only for the tail.
+            s_tokens: np.ndarray, s_valid: int,
+            ns_user_tokens: Optional[np.ndarray] = None) -> Tuple[UserCache, np.ndarray]:
+    """User side of one user: per-layer K/V for every present S row, queries only
+    for the tail; then, given ns_user_tokens [P_u, d], the user-side NS rows
+    (NS positions 0..P_u-1) and their per-layer K/V.
 
     Returns (cache, s_tail [q_{L-1}, d]).
     """
@@ -263,7 +280,19 @@ def prefill(layers: Sequence[Layer], q_sched: Sequence[int], n_heads: int, eps: 
         y = ffn(z, W.s_gf, W.s_w1, W.s_w2, eps)
         y[qpos < valid_from] = 0.0
         x, pos = y, qpos
+    if ns_user_tokens is not None and ns_user_tokens.shape[0] > 0:
+        _user_ns(layers, n_heads, eps, cache, np.array(ns_user_tokens, np.float64))
     return cache, x
+
+
+def _user_ns(layers: Sequence[Layer], n_heads: int, eps: float, cache: UserCache, tokens: np.ndarray) -> None:
+    """(Re)compute the user-side NS rows of a cache from their inputs [P_u, d]:
+    they are NS positions 0..P_u-1 of every candidate's sequence, so they see the
+    valid cached S rows of each layer and the user NS rows up to themselves."""
+    cache.ns_tokens = tokens
+    nk, nv = [], []
+    out = _ns_rows(layers, n_heads, eps, cache, tokens[None], 0, capture=(nk, nv))
+    cache.nk, cache.nv, cache.ns_out = nk, nv, out[0]
 
 
 def append(layers: Sequence[Layer], n_heads: int, eps: float, cache: UserCache,
@@ -289,47 +318,73 @@ def append(layers: Sequence[Layer], n_heads: int, eps: float, cache: UserCache,
         vis = (kpos[None, :] <= qpos[:, None]) & (kpos[None, :] >= cache.valid_from)
         z = x + attend(a @ W.s_wq.T, k, v, vis, n_heads)
         x = ffn(z, W.s_gf, W.s_w1, W.s_w2, eps)
+    if cache.n_user_ns:  # the user NS rows see the grown history: recompute them
+        _user_ns(layers, n_heads, eps, out, cache.ns_tokens)
     return out, x
+
+
+def _ns_rows(layers: Sequence[Layer], n_heads: int, eps: float, cache: UserCache, tokens: np.ndarray,
+             p0: int, capture=None) -> np.ndarray:
+    """NS rows of C independent groups against one user's cache: tokens [C, Pn, d]
+    are NS positions p0..p0+Pn-1 (private parameters of those positions). Row j
+    of a group sees every valid cached S row of the layer, every cached user NS
+    row when p0 > 0 (those are positions 0..p0-1), and its group's rows 0..j.
+    With capture = (nk, nv), the rows' K and V of each layer are appended to the
+    two lists (C must be 1). Returns the rows after the last layer [C, Pn, d]."""
+    C, Pn, d = tokens.shape
+    y = np.array(tokens, np.float64)
+    causal = np.tril(np.ones((Pn, Pn), bool))
+    ks = slice(p0, p0 + Pn)
+    for l, W in enumerate(layers):
+        n = cache.length(l)
+        s_ok = (cache.base[l] + np.arange(n)) >= cache.valid_from
+        a = np.stack([rmsnorm(y[:, j], W.ns_ga[p0 + j], eps) for j in range(Pn)], axis=1)
+        qn = np.einsum("cpi,poi->cpo", a, W.ns_wq[ks])
+        kn = np.einsum("cpi,poi->cpo", a, W.ns_wk[ks])
+        vn = np.einsum("cpi,poi->cpo", a, W.ns_wv[ks])
+        if capture is not None:
+            capture[0].append(kn[0].copy())
+            capture[1].append(vn[0].copy())
+        k_parts, v_parts, vis_parts = [cache.k[l]], [cache.v[l]], [np.broadcast_to(s_ok, (Pn, n))]
+        if p0 > 0:
+            k_parts.append(cache.nk[l]); v_parts.append(cache.nv[l]); vis_parts.append(np.ones((Pn, p0), bool))
+        keys = np.concatenate([np.broadcast_to(kp, (C,) + kp.shape) for kp in k_parts] + [kn], axis=1)
+        vals = np.concatenate([np.broadcast_to(vp, (C,) + vp.shape) for vp in v_parts] + [vn], axis=1)
+        vis = np.concatenate(vis_parts + [causal], axis=1)
+        z = y + attend(qn, keys, vals, vis, n_heads)
+        y = np.stack([ffn(z[:, j], W.ns_gf[p0 + j], W.ns_w1[p0 + j], W.ns_w2[p0 + j], eps) for j in range(Pn)], axis=1)
+    return y
 
 
 def score(layers: Sequence[Layer], n_heads: int, eps: float, cache: UserCache,
           ns_tokens: np.ndarray, chunk: int = 64) -> np.ndarray:
-    """NS side of C candidates against one user's cache: ns_tokens [C, P, d] -> [C, P, d].
+    """NS side of C candidates against one user's cache: ns_tokens [C, Pc, d] -> [C, Pc, d].
 
-    NS row k of a candidate sees every valid cached row of the layer and that
-    candidate's NS rows 0..k. Candidates are independent; they are processed
-    ``chunk`` at a time only to bound memory.
+    The candidate rows are NS positions P_u..P_u+Pc-1 (P_u = the cache's user NS
+    rows, 0 without them). Row k of a candidate sees every valid cached S row of
+    the layer, every user NS row, and that candidate's rows up to itself.
+    Candidates are independent; they are processed ``chunk`` at a time only to
+    bound memory.
     """
     C, P, d = ns_tokens.shape
     out = np.empty((C, P, d))
-    causal = np.tril(np.ones((P, P), bool))
     for c0 in range(0, C, chunk):
-        y = np.array(ns_tokens[c0:c0 + chunk], np.float64)      # [c, P, d]
-        for l, W in enumerate(layers):
-            n = cache.length(l)
-            s_ok = (cache.base[l] + np.arange(n)) >= cache.valid_from
-            a = np.stack([rmsnorm(y[:, k], W.ns_ga[k], eps) for k in range(P)], axis=1)
-            qn = np.einsum("cpi,poi->cpo", a, W.ns_wq)
-            kn = np.einsum("cpi,poi->cpo", a, W.ns_wk)
-            vn = np.einsum("cpi,poi->cpo", a, W.ns_wv)
-            keys = np.concatenate([np.broadcast_to(cache.k[l], (y.shape[0], n, d)), kn], axis=1)
-            vals = np.concatenate([np.broadcast_to(cache.v[l], (y.shape[0], n, d)), vn], axis=1)
-            vis = np.concatenate([np.broadcast_to(s_ok, (P, n)), causal], axis=1)
-            z = y + attend(qn, keys, vals, vis, n_heads)
-            y = np.stack([ffn(z[:, k], W.ns_gf[k], W.ns_w1[k], W.ns_w2[k], eps) for k in range(P)], axis=1)
-        out[c0:c0 + chunk] = y
+        out[c0:c0 + chunk] = _ns_rows(layers, n_heads, eps, cache, ns_tokens[c0:c0 + chunk], cache.n_user_ns)
     return out
 
 
 def block_forward(layers: Sequence[Layer], q_sched: Sequence[int], n_heads: int, eps: float,
-                  s_tokens: np.ndarray, s_lens: np.ndarray, ns_tokens: np.ndarray):
-    """Full pass for B users: s_tokens [B, L_S, d], s_lens [B], ns_tokens [B, C, P, d].
+                  s_tokens: np.ndarray, s_lens: np.ndarray, ns_tokens: np.ndarray,
+                  ns_user_tokens: Optional[np.ndarray] = None):
+    """Full pass for B users: s_tokens [B, L_S, d], s_lens [B], ns_tokens [B, C, Pc, d]
+    (candidate rows) and optionally ns_user_tokens [B, P_u, d] (user NS rows).
 
-    Returns (s_tail [B, q_{L-1}, d], ns_out [B, C, P, d]).
+    Returns (s_tail [B, q_{L-1}, d], ns_out [B, C, Pc, d]).
     """
     tails, outs = [], []
     for u in range(s_tokens.shape[0]):
-        cache, tail = prefill(layers, q_sched, n_heads, eps, s_tokens[u], int(s_lens[u]))
+        cache, tail = prefill(layers, q_sched, n_heads, eps, s_tokens[u], int(s_lens[u]),
+                              None if ns_user_tokens is None else ns_user_tokens[u])
         tails.append(tail)
         outs.append(score(layers, n_heads, eps, cache, ns_tokens[u]))
     return np.stack(tails), np.stack(outs)

@@ -342,6 +342,73 @@ def test_append_equals_reprefill(s_valid, m):
         np.testing.assert_allclose(np.concatenate([o_a, o_b]), new_out, rtol=1e-11, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# User-side NS fields, computed once per user and cached
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Pu,s_valid", [(2, 7), (1, 10), (4, 3)])
+def test_user_ns_cached_equals_literal(Pu, s_valid):
+    # NS positions 0..Pu-1 computed once in the user's prefill and cached; each
+    # candidate's rows Pu..P-1 scored against that cache == the literal definition
+    # over [S ; user NS ; candidate NS], candidate by candidate
+    rng = np.random.default_rng(11)
+    L, d, Fh, H, L_S, P, C = 3, 16, 32, 2, 10, 5, 3
+    lay = rand_layers(rng, L, d, Fh, P)
+    q = [8, 5, 2]
+    xs = rng.normal(size=(L_S, d))
+    un = rng.normal(size=(Pu, d))
+    cn = rng.normal(size=(C, P - Pu, d))
+    cache, tail = O.prefill(lay, q, H, EPS, xs, s_valid, un)
+    assert cache.n_user_ns == Pu and len(cache.nk) == L and cache.nk[0].shape == (Pu, d)
+    got = O.score(lay, H, EPS, cache, cn)
+    for c in range(C):
+        t_ref, n_ref, _ = O.forward_dense(lay, q, H, EPS, xs, s_valid, np.concatenate([un, cn[c]]))
+        np.testing.assert_allclose(tail, t_ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(cache.ns_out, n_ref[:Pu], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(got[c], n_ref[Pu:], rtol=1e-11, atol=1e-12)
+
+
+def test_user_ns_rows_see_candidates_nowhere():
+    # a user NS row's output does not depend on any candidate row (they come later),
+    # while every candidate row does depend on the user NS rows
+    rng = np.random.default_rng(13)
+    L, d, Fh, H, L_S, P, Pu = 2, 16, 32, 2, 8, 4, 2
+    lay = rand_layers(rng, L, d, Fh, P)
+    xs = rng.normal(size=(L_S, d))
+    un = rng.normal(size=(Pu, d))
+    cn = rng.normal(size=(P - Pu, d))
+    _, n1, _ = O.forward_dense(lay, [L_S] * L, H, EPS, xs, L_S, np.concatenate([un, cn]))
+    _, n2, _ = O.forward_dense(lay, [L_S] * L, H, EPS, xs, L_S, np.concatenate([un, cn + 1.0]))
+    np.testing.assert_array_equal(n1[:Pu], n2[:Pu])
+    un2 = un.copy(); un2[0] += 1.0
+    _, n3, _ = O.forward_dense(lay, [L_S] * L, H, EPS, xs, L_S, np.concatenate([un2, cn]))
+    assert np.all(np.abs(n3[Pu:] - n1[Pu:]).max(axis=1) > 1e-6)
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_user_ns_append_equals_reprefill(m):
+    # appended events change what the user NS rows see: append recomputes them, and
+    # the result equals a prefill of the longer history with the same user fields
+    rng = np.random.default_rng(12)
+    L, d, Fh, H, L_S, P, Pu = 2, 16, 32, 2, 12, 4, 2
+    lay = rand_layers(rng, L, d, Fh, P)
+    q, s_valid = [10, 4], 9
+    xs = rng.normal(size=(L_S, d))
+    un = rng.normal(size=(Pu, d))
+    new = rng.normal(size=(m, d))
+    cn = rng.normal(size=(3, P - Pu, d))
+    cache, _ = O.prefill(lay, q, H, EPS, xs, s_valid, un)
+    cache2, _ = O.append(lay, H, EPS, cache, new)
+    ref, _ = O.prefill(lay, [x + m for x in q], H, EPS, np.concatenate([xs, new]), s_valid + m, un)
+    np.testing.assert_allclose(cache2.ns_out, ref.ns_out, rtol=1e-11, atol=1e-12)
+    for l in range(L):
+        np.testing.assert_allclose(cache2.nk[l], ref.nk[l], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(cache2.nv[l], ref.nv[l], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(O.score(lay, H, EPS, cache2, cn), O.score(lay, H, EPS, ref, cn), rtol=1e-11, atol=1e-12)
+    # and the appended history did change the user NS rows
+    assert np.abs(cache2.ns_out - cache.ns_out).max() > 1e-6
+
+
 def test_candidates_are_independent_and_permutation_equivariant():
     wl = TINY.with_(n_candidates=6)
     lay, s, lens, ns = _gen_case(wl, seed=11)
