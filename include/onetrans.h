@@ -14,7 +14,12 @@
  *     and values cover all S rows that enter the layer;
  *   - the S side never sees NS tokens, so its per-layer K/V is computed once per
  *     user, cached, extended by newly arrived events, and shared by every
- *     candidate; only the NS side runs per candidate.
+ *     candidate; only the NS side runs per candidate. The user side also covers
+ *     profile fields (asterzephyr.xyz, design four): the first n_ns_user NS
+ *     positions may hold user fields, which depend on the user only, so they
+ *     are computed once in the prefill and their K/V is cached beside the S
+ *     side's; a candidate's rows (positions n_ns_user..n_ns-1) see them as
+ *     earlier NS rows.
  * Readings where the pages are silent: no biases; no output projection (heads
  * are concatenated into the residual); score scale 1/sqrt(head_dim); RMSNorm
  * x / sqrt(mean(x^2) + eps) * g; FFN = W2 GELU_erf(W1 x) with a residual; no
@@ -75,13 +80,15 @@ typedef enum { ONETRANS_W_BF16 = 0, ONETRANS_W_FP8_E4M3 = 1 } onetrans_wdtype;
  * the last q_sched[l] S rows; layer l's input has n_l = s_len (l = 0) or
  * q_sched[l-1] rows); append_cap >= 0 (events a cache can take after its
  * prefill); rms_eps > 0; ns_wdtype one of onetrans_wdtype (S weights are always
- * bf16). */
+ * bf16); 0 <= n_ns_user <= n_ns (user-side NS positions, computed in the
+ * prefill; 0: every NS position belongs to the candidate). */
 typedef struct onetrans_config {
   int32_t n_layers, d_model, n_heads, ffn_hidden, n_ns, s_len;
   int32_t q_sched[ONETRANS_MAX_LAYERS];
   int32_t append_cap;
   float rms_eps;
   int32_t ns_wdtype;
+  int32_t n_ns_user;
 } onetrans_config;
 
 /* One layer's parameters as the caller holds them (dev pointers, read only).
@@ -100,11 +107,13 @@ typedef struct onetrans_layer_weights {
   const float *ns_g_attn, *ns_g_ffn;
 } onetrans_layer_weights;
 
-/* A per-user, per-layer S-side K/V cache living in one caller-owned device
+/* A per-user, per-layer user-side K/V cache living in one caller-owned device
  * buffer (layout private to the library; it is plain device memory, so it can
  * be copied, saved and restored byte for byte together with this struct).
- * Layer l holds n_l + append_cap rows per user; rows [0, n_l + n_appended) are
- * filled. Fields are set by onetrans_kv_cache_init and updated by the calls. */
+ * Layer l holds n_l + append_cap S rows per user; rows [0, n_l + n_appended) are
+ * filled. With n_ns_user > 0 it also holds, per layer and user, the K/V of the
+ * user-side NS rows and the user-side NS inputs (for the recompute after an
+ * append). Fields are set by onetrans_kv_cache_init and updated by the calls. */
 typedef struct onetrans_kv_cache {
   void* buf;            /* dev, onetrans_kv_cache_bytes(cfg, n_users) bytes */
   size_t bytes;
@@ -144,18 +153,22 @@ size_t onetrans_workspace_bytes(const onetrans_config* cfg, int32_t max_users,
 
 /* User prefill: runs the S side of B users through every layer, writes each
  * layer's K/V (all n_l input rows) into `cache` and returns the last layer's
- * S outputs.
+ * S outputs; then, with n_ns_user > 0, runs each user's user-side NS rows
+ * (NS positions 0..n_ns_user-1, after every S row) and caches their K/V too.
  *   s_tokens  dev bf16 [B][s_len][d]; user u's history is right-aligned: its
  *             s_lens[u] events sit in slots [s_len - s_lens[u], s_len); the
  *             padding slots' contents are ignored (treated as zero)
  *   s_lens    dev int32 [B]; values are clamped to [0, s_len]
+ *   ns_user_tokens dev bf16 [B][n_ns_user][d]; must be NULL iff n_ns_user == 0
  *   s_out     dev fp32 [B][q_sched[L-1]][d]; rows of padding slots are 0
+ *   ns_user_out dev fp32 [B][n_ns_user][d]: the user NS rows after the last
+ *             layer, or NULL (not returned)
  * The cache must have been initialised for at least B users; it is reset
  * (n_appended = 0, prefilled = 1). */
 int onetrans_user_prefill(const onetrans_config* cfg, const void* packed,
                           const uint16_t* s_tokens, const int32_t* s_lens, int32_t B,
-                          onetrans_kv_cache* cache, float* s_out,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+                          const uint16_t* ns_user_tokens, onetrans_kv_cache* cache, float* s_out,
+                          float* ns_user_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* KV append: m newly arrived events per user (for all cache->n_users users)
  * enter every layer as queries at the next global positions; each sees the
@@ -163,16 +176,19 @@ int onetrans_user_prefill(const onetrans_config* cfg, const void* packed,
  * appended in place and cache->n_appended grows by m (host-side, at enqueue).
  *   new_tokens dev bf16 [B][m][d], B = cache->n_users
  *   new_out    dev fp32 [B][m][d]: the new events' outputs after the last layer
+ * With n_ns_user > 0 the user-side NS rows see the grown history, so their
+ * cached K/V is recomputed from the inputs the prefill kept.
  * Returns ONETRANS_ERR_CAPACITY if n_appended + m > cfg->append_cap. */
 int onetrans_kv_append(const onetrans_config* cfg, const void* packed,
                        const uint16_t* new_tokens, int32_t m, onetrans_kv_cache* cache,
                        float* new_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Candidate scoring: the NS side of C candidates of user `user` against that
- * user's cached S-side K/V (cross-request KV sharing).
- *   ns_tokens dev bf16 [C][n_ns][d]
- *   ns_out    dev fp32 [C][n_ns][d]: NS rows after the last layer
- * C may be 0 (no work). */
+ * user's cached user-side K/V (cross-request KV sharing). A candidate has
+ * Pc = n_ns - n_ns_user rows, NS positions n_ns_user..n_ns-1.
+ *   ns_tokens dev bf16 [C][Pc][d]
+ *   ns_out    dev fp32 [C][Pc][d]: the candidate rows after the last layer
+ * C may be 0 (no work); so may Pc. */
 int onetrans_score_candidates(const onetrans_config* cfg, const void* packed,
                               const onetrans_kv_cache* cache, int32_t user,
                               const uint16_t* ns_tokens, int32_t C, float* ns_out,
@@ -180,19 +196,23 @@ int onetrans_score_candidates(const onetrans_config* cfg, const void* packed,
 
 /* Full pass without a persistent cache: prefill of B users into a cache held
  * in the workspace, then scoring of each user's C candidates.
- *   s_tokens, s_lens, s_out as in onetrans_user_prefill
- *   ns_tokens dev bf16 [B][C][n_ns][d], ns_out dev fp32 [B][C][n_ns][d]
+ *   s_tokens, s_lens, ns_user_tokens, s_out as in onetrans_user_prefill
+ *   ns_tokens dev bf16 [B][C][Pc][d], ns_out dev fp32 [B][C][Pc][d]
+ *   (Pc = n_ns - n_ns_user)
  * Size the workspace with onetrans_block_forward_workspace_bytes (the cache plus
- * separate prefill and scoring areas). The S side runs on `stream`; the NS side
- * runs concurrently on a second stream that the library creates on first use for
- * the calling thread and device (default priority, kept until the process
- * ends), and NS layer l waits only for the S side's layer-l cache rows. Work
- * queued on `stream` after the call waits for both sides. */
+ * separate prefill and scoring areas). Without user-side NS rows the S side
+ * runs on `stream` and the NS side concurrently on a second stream that the
+ * library creates on first use for the calling thread and device (default
+ * priority, kept until the process ends); NS layer l waits only for the S
+ * side's layer-l cache rows. With user-side NS rows both run on `stream`, the
+ * candidates after the whole user side. Work queued on `stream` after the call
+ * waits for everything. */
 size_t onetrans_block_forward_workspace_bytes(const onetrans_config* cfg, int32_t B, int32_t C);
 int onetrans_block_forward(const onetrans_config* cfg, const void* packed,
                            const uint16_t* s_tokens, const int32_t* s_lens, int32_t B,
-                           const uint16_t* ns_tokens, int32_t C, float* s_out, float* ns_out,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+                           const uint16_t* ns_user_tokens, const uint16_t* ns_tokens, int32_t C,
+                           float* s_out, float* ns_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /* ---- diagnostics --------------------------------------------------------- */
 

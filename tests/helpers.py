@@ -19,10 +19,10 @@ def weights(wl: Workload, seed: int = 0, private_gains: bool = False):
     return raw, O.layers_from_arrays(raw)
 
 
-def config(wl: Workload, append_cap: int = 0):
+def config(wl: Workload, append_cap: int = 0, n_ns_user: int = 0):
     from unified_transformer_recommender_onetrans_amd import make_config
     return make_config(wl.n_layers, wl.d_model, wl.n_heads, wl.ffn_hidden, wl.n_ns, wl.s_len, wl.q_sched,
-                       append_cap=append_cap, rms_eps=wl.rms_eps, ns_wdtype=wl.ns_wdtype)
+                       append_cap=append_cap, rms_eps=wl.rms_eps, ns_wdtype=wl.ns_wdtype, n_ns_user=n_ns_user)
 
 
 def bf16_dev(a: np.ndarray, device="cuda"):
@@ -48,10 +48,11 @@ def device_weights(raw, device="cuda"):
     return out
 
 
-def model(wl: Workload, seed: int = 0, append_cap: int = 0, private_gains: bool = False, device="cuda"):
+def model(wl: Workload, seed: int = 0, append_cap: int = 0, private_gains: bool = False, device="cuda",
+          n_ns_user: int = 0):
     from unified_transformer_recommender_onetrans_amd import OneTrans
     raw, lay = weights(wl, seed, private_gains)
-    return OneTrans(config(wl, append_cap), device_weights(raw, device), device=device), lay
+    return OneTrans(config(wl, append_cap, n_ns_user), device_weights(raw, device), device=device), lay
 
 
 def errors(got, ref):

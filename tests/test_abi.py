@@ -129,10 +129,10 @@ def test_compute_calls_reject_bad_arguments(lib):
     c = _cache(lib, cfg)
     big = 1 << 40
     # prefill
-    assert lib.onetrans_user_prefill(ctypes.byref(cfg), None, F, F, 1, ctypes.byref(c), F, F, big, None) == INVALID
-    assert lib.onetrans_user_prefill(ctypes.byref(cfg), F, F, F, 3, ctypes.byref(c), F, F, big, None) == INVALID
-    assert lib.onetrans_user_prefill(ctypes.byref(cfg), F, F, F, 1, ctypes.byref(c), F + 4, F, big, None) == INVALID
-    assert lib.onetrans_user_prefill(ctypes.byref(cfg), F, F, F, 2, ctypes.byref(c), F, F, 1024, None) == WORKSPACE
+    assert lib.onetrans_user_prefill(ctypes.byref(cfg), None, F, F, 1, None, ctypes.byref(c), F, None, F, big, None) == INVALID
+    assert lib.onetrans_user_prefill(ctypes.byref(cfg), F, F, F, 3, None, ctypes.byref(c), F, None, F, big, None) == INVALID
+    assert lib.onetrans_user_prefill(ctypes.byref(cfg), F, F, F, 1, None, ctypes.byref(c), F + 4, None, F, big, None) == INVALID
+    assert lib.onetrans_user_prefill(ctypes.byref(cfg), F, F, F, 2, None, ctypes.byref(c), F, None, F, 1024, None) == WORKSPACE
     # append
     assert lib.onetrans_kv_append(ctypes.byref(cfg), F, F, 65, ctypes.byref(c), F, F, big, None) == CAPACITY
     c2 = _cache(lib, cfg, n_appended=60)
@@ -151,9 +151,9 @@ def test_compute_calls_reject_bad_arguments(lib):
     assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(c), 0, F, 0, F, F, big, None) == OK
     assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(c), 0, F + 2, 8, F, F, big, None) == INVALID
     # block_forward
-    assert lib.onetrans_block_forward(ctypes.byref(cfg), F, F, F, 0, F, 4, F, F, F, big, None) == INVALID
-    assert lib.onetrans_block_forward(ctypes.byref(cfg), F, F, F, 1, F, 4, F, F, F, 10, None) == WORKSPACE
-    assert lib.onetrans_block_forward(ctypes.byref(cfg), F, F, F, 1, None, 4, F, None, F, big, None) == INVALID
+    assert lib.onetrans_block_forward(ctypes.byref(cfg), F, F, F, 0, None, F, 4, F, F, F, big, None) == INVALID
+    assert lib.onetrans_block_forward(ctypes.byref(cfg), F, F, F, 1, None, F, 4, F, F, F, 10, None) == WORKSPACE
+    assert lib.onetrans_block_forward(ctypes.byref(cfg), F, F, F, 1, None, None, 4, F, None, F, big, None) == INVALID
     # cache read
     assert lib.onetrans_kv_cache_read(ctypes.byref(cfg), ctypes.byref(c), 8, 0, 1, F, F, None) == INVALID
     assert lib.onetrans_kv_cache_read(ctypes.byref(cfg), ctypes.byref(c), 0, 0, 1501, F, F, None) == INVALID
@@ -163,6 +163,34 @@ def test_compute_calls_reject_bad_arguments(lib):
     need = lib.onetrans_packed_weight_bytes(ctypes.byref(cfg))
     assert lib.onetrans_pack_weights(ctypes.byref(cfg), lw, F, need - 1, None) == WORKSPACE
     assert lib.onetrans_pack_weights(ctypes.byref(cfg), lw, F, need, None) == INVALID  # NULL weight pointers
+
+
+def test_user_ns_rows_validation(lib):
+    # n_ns_user: range check, a larger cache, and the user tokens given exactly when > 0
+    cfg = l_cfg()
+    base = lib.onetrans_kv_cache_bytes(ctypes.byref(cfg), 2)
+    cfg.n_ns_user = cfg.n_ns + 1
+    assert lib.onetrans_check_config(ctypes.byref(cfg)) == UNSUPPORTED
+    cfg.n_ns_user = -1
+    assert lib.onetrans_check_config(ctypes.byref(cfg)) == UNSUPPORTED
+    cfg.n_ns_user = 8
+    assert lib.onetrans_check_config(ctypes.byref(cfg)) == OK
+    d = cfg.d_model
+    grown = lib.onetrans_kv_cache_bytes(ctypes.byref(cfg), 2)
+    assert grown >= base + 2 * 8 * d * 2 * (2 * cfg.n_layers + 1)
+    F = 1 << 41
+    big = 1 << 40
+    c = _cache(lib, cfg)
+    assert lib.onetrans_user_prefill(ctypes.byref(cfg), F, F, F, 1, None, ctypes.byref(c), F, None, F, big, None) == INVALID
+    assert lib.onetrans_user_prefill(ctypes.byref(cfg), F, F, F, 1, F + 8, ctypes.byref(c), F, None, F, big, None) == INVALID
+    assert lib.onetrans_block_forward(ctypes.byref(cfg), F, F, F, 1, None, F, 4, F, F, F, big, None) == INVALID
+    cfg0 = l_cfg()
+    c0 = _cache(lib, cfg0)
+    assert lib.onetrans_user_prefill(ctypes.byref(cfg0), F, F, F, 1, F, ctypes.byref(c0), F, None, F, big, None) == INVALID
+    # all NS positions user-side: a candidate has no rows, scoring does nothing
+    cfg.n_ns_user = cfg.n_ns
+    c1 = _cache(lib, cfg)
+    assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(c1), 0, F, 8, F, F, big, None) == OK
 
 
 def test_status_strings(lib):

@@ -138,6 +138,76 @@ def test_peaked_attention_moves_softmax_reference():
     assert_close(ns_out[0, 0, 0].cpu().numpy(), ref_n[0, 0, 0], wl.ns_wdtype, "NS row of the peaked query")
 
 
+# user-side NS rows: (workload, histories, n_ns_user)
+USER_NS = {
+    "b_dh64_P32_u8": (SMALL["b_dh64_P32"][0], [200, 1], 8),
+    "a_dh32_P5_u2": (SMALL["a_dh32_P5"][0], [300, 41, 0], 2),
+    "c_fp8_u4": (SMALL["c_fp8"][0], [150, 200], 4),
+}
+
+
+def _user_inputs(wl, lens, Pu):
+    s, lens, ns = _inputs(wl, lens)
+    rng = np.random.default_rng(21)
+    un = rng.standard_normal((s.shape[0], Pu, wl.d_model)).astype(np.float32)
+    un = torch.from_numpy(un).to(torch.bfloat16).float().numpy()  # bf16 values, as both sides consume
+    return s, lens, np.ascontiguousarray(ns[:, :, Pu:]), un
+
+
+@pytest.mark.parametrize("name", list(USER_NS))
+def test_user_ns_block_forward_matches_oracle(name):
+    wl, lens, Pu = USER_NS[name]
+    print(f"case {name}", flush=True)
+    m, lay = model(wl, private_gains=(name == "c_fp8_u4"), n_ns_user=Pu)
+    s, lens, cn, un = _user_inputs(wl, lens, Pu)
+    s_out, ns_out = m.block_forward(*_dev(s, lens, cn), ns_user_tokens=bf16_dev(un))
+    torch.cuda.synchronize()
+    ref_t, ref_n = O.block_forward(lay, wl.q_sched, wl.n_heads, EPS, s, lens, cn, un)
+    assert ns_out.shape == (s.shape[0], cn.shape[1], wl.n_ns - Pu, wl.d_model)
+    assert_close(s_out.cpu().numpy(), ref_t, wl.ns_wdtype, "S tail")
+    assert_close(ns_out.cpu().numpy(), ref_n, wl.ns_wdtype, "candidate NS out")
+
+
+@pytest.mark.parametrize("name", ["b_dh64_P32_u8", "a_dh32_P5_u2"])
+def test_user_ns_prefill_append_score_match_oracle(name):
+    wl, lens, Pu = USER_NS[name]
+    print(f"case {name}", flush=True)
+    m1 = 9
+    mdl, lay = model(wl, append_cap=m1, n_ns_user=Pu)
+    s, lens, cn, un = _user_inputs(wl, lens, Pu)
+    sd, ld, nd = _dev(s, lens, cn)
+    B = s.shape[0]
+    cache = mdl.new_cache(B)
+    _, un_out = mdl.user_prefill(sd, ld, cache, ns_user_tokens=bf16_dev(un), return_user_ns=True)
+    before = [mdl.score_candidates(cache, u, nd[u]) for u in range(B)]
+    new1 = make_append_tokens(wl, m=m1)
+    mdl.kv_append(bf16_dev(new1), cache)
+    after = [mdl.score_candidates(cache, u, nd[u]) for u in range(B)]
+    torch.cuda.synchronize()
+    for u in range(B):
+        oc, _ = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[u], int(lens[u]), un[u])
+        assert_close(un_out[u].cpu().numpy(), oc.ns_out, wl.ns_wdtype, f"user {u} user NS rows")
+        assert_close(before[u].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, cn[u]), wl.ns_wdtype,
+                     f"user {u} score")
+        oc2, _ = O.append(lay, wl.n_heads, EPS, oc, new1[u])
+        assert_close(after[u].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc2, cn[u]), wl.ns_wdtype,
+                     f"user {u} score after append")
+
+
+def test_user_ns_score_equals_block_forward():
+    # the same kernels on the same inputs: scoring against a prefilled cache reproduces
+    # block_forward bit for bit, also with user-side NS rows
+    wl, lens, Pu = USER_NS["b_dh64_P32_u8"]
+    mdl, _ = model(wl, n_ns_user=Pu)
+    s, lens, cn, un = _user_inputs(wl, lens, Pu)
+    sd, ld, nd = _dev(s, lens, cn)
+    _, ns_bf = mdl.block_forward(sd, ld, nd, ns_user_tokens=bf16_dev(un))
+    cache = mdl.new_cache(s.shape[0])
+    mdl.user_prefill(sd, ld, cache, ns_user_tokens=bf16_dev(un))
+    for u in range(s.shape[0]):
+        assert torch.equal(mdl.score_candidates(cache, u, nd[u]), ns_bf[u])
+
+
 def test_zero_candidates_and_capacity_errors():
     from unified_transformer_recommender_onetrans_amd import OneTransError
     wl, lens = SMALL["b_dh64_P32"]

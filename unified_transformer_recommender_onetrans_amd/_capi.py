@@ -18,7 +18,7 @@ class Config(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("ffn_hidden", ctypes.c_int32), ("n_ns", ctypes.c_int32), ("s_len", ctypes.c_int32),
                 ("q_sched", ctypes.c_int32 * MAX_LAYERS), ("append_cap", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("ns_wdtype", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("ns_wdtype", ctypes.c_int32), ("n_ns_user", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -46,8 +46,9 @@ EXPORTS = {
     "onetrans_block_forward_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Config), ctypes.c_int32,
                                                                  ctypes.c_int32]),
     "onetrans_user_prefill": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_void_p, ctypes.c_void_p,
-                                             ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(KVCache),
-                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.POINTER(KVCache), ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "onetrans_kv_append": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                           ctypes.POINTER(KVCache), ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]),
@@ -55,9 +56,9 @@ EXPORTS = {
                                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "onetrans_block_forward": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_void_p, ctypes.c_void_p,
-                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
-                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                              ctypes.c_void_p]),
+                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_size_t, ctypes.c_void_p]),
     "onetrans_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "onetrans_last_error": (ctypes.c_char_p, []),
     "onetrans_kv_cache_read": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(KVCache), ctypes.c_int32,

@@ -20,7 +20,7 @@ WEIGHT_KEYS = ("s_wqkv", "s_w1", "s_w2", "s_g_attn", "s_g_ffn", "ns_wqkv", "ns_w
 
 def make_config(n_layers: int, d_model: int, n_heads: int, ffn_hidden: int, n_ns: int, s_len: int,
                 q_sched: Sequence[int], append_cap: int = 0, rms_eps: float = 1e-6,
-                ns_wdtype: str = "bf16") -> C.Config:
+                ns_wdtype: str = "bf16", n_ns_user: int = 0) -> C.Config:
     if len(q_sched) != n_layers:
         raise ValueError("q_sched needs one entry per layer")
     if n_layers > C.MAX_LAYERS:
@@ -31,6 +31,7 @@ def make_config(n_layers: int, d_model: int, n_heads: int, ffn_hidden: int, n_ns
     for i, q in enumerate(q_sched):
         cfg.q_sched[i] = int(q)
     cfg.ns_wdtype = {"bf16": C.W_BF16, "e4m3": C.W_FP8_E4M3}[ns_wdtype]
+    cfg.n_ns_user = n_ns_user
     return cfg
 
 
@@ -129,18 +130,41 @@ class OneTrans:
     def new_cache(self, n_users: int) -> KVCache:
         return KVCache(self.cfg, n_users, self.device)
 
+    @property
+    def n_cand_ns(self) -> int:
+        """NS rows per candidate (the positions after the user-side ones)."""
+        return self.cfg.n_ns - self.cfg.n_ns_user
+
+    def _user_ns(self, t: Optional[torch.Tensor], B: int) -> Optional[int]:
+        Pu = self.cfg.n_ns_user
+        if Pu == 0:
+            if t is not None:
+                raise ValueError("ns_user_tokens given but the config has n_ns_user = 0")
+            return None
+        if t is None:
+            raise ValueError(f"ns_user_tokens [B, {Pu}, d] required (n_ns_user = {Pu})")
+        _expect(t, "ns_user_tokens", (B, Pu, self.cfg.d_model), torch.bfloat16, self.device)
+        return t.data_ptr()
+
     # -- the four entry points --
-    def user_prefill(self, s_tokens: torch.Tensor, s_lens: torch.Tensor, cache: KVCache) -> torch.Tensor:
+    def user_prefill(self, s_tokens: torch.Tensor, s_lens: torch.Tensor, cache: KVCache,
+                     ns_user_tokens: Optional[torch.Tensor] = None, return_user_ns: bool = False):
+        """S side (and the user-side NS rows) of B users into `cache`. Returns the S tail,
+        and with return_user_ns also the user NS rows' outputs [B, n_ns_user, d]."""
         cfg = self.cfg
         B = s_tokens.shape[0]
         _expect(s_tokens, "s_tokens", (B, cfg.s_len, cfg.d_model), torch.bfloat16, self.device)
         _expect(s_lens, "s_lens", (B,), torch.int32, self.device)
+        un = self._user_ns(ns_user_tokens, B)
         out = torch.empty(B, cfg.q_sched[cfg.n_layers - 1], cfg.d_model, dtype=torch.float32, device=self.device)
+        un_out = (torch.empty(B, cfg.n_ns_user, cfg.d_model, dtype=torch.float32, device=self.device)
+                  if return_user_ns and cfg.n_ns_user > 0 else None)
         ws = self.workspace(lib().onetrans_workspace_bytes(ctypes.byref(cfg), B, 0, 0))
         check(lib().onetrans_user_prefill(ctypes.byref(cfg), self.packed.data_ptr(), s_tokens.data_ptr(),
-                                          s_lens.data_ptr(), B, ctypes.byref(cache.c), out.data_ptr(),
-                                          ws.data_ptr(), ws.numel(), _stream(self.device)), "user_prefill")
-        return out
+                                          s_lens.data_ptr(), B, un, ctypes.byref(cache.c), out.data_ptr(),
+                                          _ptr(un_out), ws.data_ptr(), ws.numel(), _stream(self.device)),
+              "user_prefill")
+        return (out, un_out) if return_user_ns else out
 
     def kv_append(self, new_tokens: torch.Tensor, cache: KVCache) -> torch.Tensor:
         cfg = self.cfg
@@ -156,28 +180,30 @@ class OneTrans:
     def score_candidates(self, cache: KVCache, user: int, ns_tokens: torch.Tensor,
                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
         cfg = self.cfg
-        Cn = ns_tokens.shape[0]
-        _expect(ns_tokens, "ns_tokens", (Cn, cfg.n_ns, cfg.d_model), torch.bfloat16, self.device)
+        Cn, Pc = ns_tokens.shape[0], self.n_cand_ns
+        _expect(ns_tokens, "ns_tokens", (Cn, Pc, cfg.d_model), torch.bfloat16, self.device)
         if out is None:
-            out = torch.empty(Cn, cfg.n_ns, cfg.d_model, dtype=torch.float32, device=self.device)
-        _expect(out, "ns_out", (Cn, cfg.n_ns, cfg.d_model), torch.float32, self.device)
+            out = torch.empty(Cn, Pc, cfg.d_model, dtype=torch.float32, device=self.device)
+        _expect(out, "ns_out", (Cn, Pc, cfg.d_model), torch.float32, self.device)
         ws = self.workspace(lib().onetrans_workspace_bytes(ctypes.byref(cfg), 0, Cn, 0))
         check(lib().onetrans_score_candidates(ctypes.byref(cfg), self.packed.data_ptr(), ctypes.byref(cache.c), user,
                                               ns_tokens.data_ptr(), Cn, out.data_ptr(), ws.data_ptr(), ws.numel(),
                                               _stream(self.device)), "score_candidates")
         return out
 
-    def block_forward(self, s_tokens: torch.Tensor, s_lens: torch.Tensor, ns_tokens: torch.Tensor):
+    def block_forward(self, s_tokens: torch.Tensor, s_lens: torch.Tensor, ns_tokens: torch.Tensor,
+                      ns_user_tokens: Optional[torch.Tensor] = None):
         cfg = self.cfg
-        B, Cn = ns_tokens.shape[0], ns_tokens.shape[1]
+        B, Cn, Pc = ns_tokens.shape[0], ns_tokens.shape[1], self.n_cand_ns
         _expect(s_tokens, "s_tokens", (B, cfg.s_len, cfg.d_model), torch.bfloat16, self.device)
         _expect(s_lens, "s_lens", (B,), torch.int32, self.device)
-        _expect(ns_tokens, "ns_tokens", (B, Cn, cfg.n_ns, cfg.d_model), torch.bfloat16, self.device)
+        _expect(ns_tokens, "ns_tokens", (B, Cn, Pc, cfg.d_model), torch.bfloat16, self.device)
+        un = self._user_ns(ns_user_tokens, B)
         s_out = torch.empty(B, cfg.q_sched[cfg.n_layers - 1], cfg.d_model, dtype=torch.float32, device=self.device)
-        ns_out = torch.empty(B, Cn, cfg.n_ns, cfg.d_model, dtype=torch.float32, device=self.device)
+        ns_out = torch.empty(B, Cn, Pc, cfg.d_model, dtype=torch.float32, device=self.device)
         ws = self.workspace(lib().onetrans_block_forward_workspace_bytes(ctypes.byref(cfg), B, Cn))
         check(lib().onetrans_block_forward(ctypes.byref(cfg), self.packed.data_ptr(), s_tokens.data_ptr(),
-                                           s_lens.data_ptr(), B, ns_tokens.data_ptr(), Cn, s_out.data_ptr(),
+                                           s_lens.data_ptr(), B, un, ns_tokens.data_ptr(), Cn, s_out.data_ptr(),
                                            ns_out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(self.device)),
               "block_forward")
         return s_out, ns_out

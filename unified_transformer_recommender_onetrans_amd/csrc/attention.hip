@@ -630,20 +630,13 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
 
   if (kh == 0 && wave_live) {
-    // the candidate's own NS keys: query g = c*P + k sees g' in [c*P, g];
-    // NS K and V are row-major [H][nq][dh]
-    const int P = p.P;
-    const int g_lo = (wq0 / P) * P;
-    const int g_hi = min(wq0 + 31, p.nq - 1);
-    const int my_first = (qi / P) * P;
-    const __bf16* knb = p.kn + h * p.kn_head_stride;
-    const __bf16* vnb = p.vn + h * p.kn_head_stride;
-#pragma unroll 1
-    for (int t0 = g_lo; t0 <= g_hi; t0 += 32) {
+    // 32 keys [t0, t0 + 32) of a row-major K / V block (rows past n_rows - 1 are read as
+    // that row and masked), visible to this lane when vis(key) holds
+    auto key_block = [&](const __bf16* knb, const __bf16* vnb, int n_rows, int t0, auto vis) {
       f32x16 sk[1];
 #pragma unroll
       for (int j = 0; j < 16; ++j) sk[0][j] = 0.f;
-      const int krow = min(t0 + l32, p.nq - 1);
+      const int krow = min(t0 + l32, n_rows - 1);
 #pragma unroll
       for (int s = 0; s < DH / 16; ++s) {
         const bf16x8 a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
@@ -652,8 +645,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = t0 + 8 * (j >> 2) + half * 4 + (j & 3);
-        const bool vis = q_ok && key <= qi && key >= my_first;
-        if (!vis) sk[0][j] = -INFINITY;
+        if (!(q_ok && vis(key))) sk[0][j] = -INFINITY;
       }
       bf16x8 pk[1][2];
       softmax_update<DH, 1>(st, sk, pk, p.scale_log2);
@@ -664,12 +656,30 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
           bf16x8 a;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), p.nq - 1);
+            const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), n_rows - 1);
             a[i] = vnb[(long)key * DH + db * 32 + l32];
           }
           st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][c], st.o[db], 0, 0, 0);
         }
+    };
+    // the user's cached NS rows: earlier NS positions, seen in full by every query
+    if (p.n_x > 0) {
+      const __bf16* xkb = p.xk + h * p.x_head_stride;
+      const __bf16* xvb = p.xv + h * p.x_head_stride;
+      const int n_x = p.n_x;
+#pragma unroll 1
+      for (int t0 = 0; t0 < n_x; t0 += 32) key_block(xkb, xvb, n_x, t0, [&](int key) { return key < n_x; });
     }
+    // the candidate's own NS keys: query g = c*P + k sees g' in [c*P, g];
+    // NS K and V are row-major [H][nq][dh]
+    const int P = p.P;
+    const int g_lo = (wq0 / P) * P;
+    const int g_hi = min(wq0 + 31, p.nq - 1);
+    const int my_first = (qi / P) * P;
+#pragma unroll 1
+    for (int t0 = g_lo; t0 <= g_hi; t0 += 32)
+      key_block(p.kn + h * p.kn_head_stride, p.vn + h * p.kn_head_stride, p.nq, t0,
+                [&](int key) { return key <= qi && key >= my_first; });
   }
 
   // ---- merge the two key halves of each query block (LDS of the tile ring is free) ----

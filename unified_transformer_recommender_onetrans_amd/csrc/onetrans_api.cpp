@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -27,6 +28,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 struct Shape {
   int L, d, H, dh, F, P, s_len, append_cap;
+  int Pu, Pc;  // user-side NS positions 0..Pu-1; a candidate's rows Pu..P-1 (Pc of them)
   int q[ONETRANS_MAX_LAYERS], n[ONETRANS_MAX_LAYERS], cap[ONETRANS_MAX_LAYERS];
   bool fp8;
   float eps;
@@ -49,7 +51,9 @@ int make_shape(const onetrans_config* c, Shape& s) {
   if (!(c->rms_eps > 0.f) || !isfinite(c->rms_eps)) return fail(ONETRANS_ERR_INVALID_ARG, "rms_eps must be positive and finite");
   if (c->ns_wdtype != ONETRANS_W_BF16 && c->ns_wdtype != ONETRANS_W_FP8_E4M3)
     return fail(ONETRANS_ERR_UNSUPPORTED, "ns_wdtype must be ONETRANS_W_BF16 or ONETRANS_W_FP8_E4M3");
+  if (c->n_ns_user < 0 || c->n_ns_user > c->n_ns) return fail(ONETRANS_ERR_UNSUPPORTED, "n_ns_user must be in [0, n_ns]");
   s.L = c->n_layers; s.d = c->d_model; s.H = c->n_heads; s.dh = dh; s.F = c->ffn_hidden; s.P = c->n_ns;
+  s.Pu = c->n_ns_user; s.Pc = c->n_ns - c->n_ns_user;
   s.s_len = c->s_len; s.append_cap = c->append_cap; s.fp8 = c->ns_wdtype == ONETRANS_W_FP8_E4M3; s.eps = c->rms_eps;
   int prev = c->s_len;
   for (int l = 0; l < s.L; ++l) {
@@ -92,8 +96,13 @@ size_t packed_layout(const Shape& s, LayerOffsets* lo) {
 }
 
 // Cache buffer: valid_from int32 [B], then per layer K bf16 [B][H][cap_l][dh]
-// and V^T bf16 [B][H][dh][cap_l].
-size_t cache_layout(const Shape& s, int B, size_t* k_off, size_t* v_off) {
+// and V^T bf16 [B][H][dh][cap_l]; with user-side NS rows, per layer their K and V
+// bf16 [B][H][Pu][dh] (row-major, as the NS attention reads own keys), then their
+// inputs bf16 [B][Pu][d].
+struct UserNsOff {
+  size_t k[ONETRANS_MAX_LAYERS], v[ONETRANS_MAX_LAYERS], tok;
+};
+size_t cache_layout(const Shape& s, int B, size_t* k_off, size_t* v_off, UserNsOff* un = nullptr) {
   size_t off = align_up((size_t)B * 4);
   for (int l = 0; l < s.L; ++l) {
     const size_t blk = (size_t)B * s.H * s.cap[l] * s.dh * 2;
@@ -101,6 +110,17 @@ size_t cache_layout(const Shape& s, int B, size_t* k_off, size_t* v_off) {
     off = align_up(off + blk);
     if (v_off) v_off[l] = off;
     off = align_up(off + blk);
+  }
+  if (s.Pu > 0) {
+    const size_t blk = (size_t)B * s.H * s.Pu * s.dh * 2;
+    for (int l = 0; l < s.L; ++l) {
+      if (un) un->k[l] = off;
+      off = align_up(off + blk);
+      if (un) un->v[l] = off;
+      off = align_up(off + blk);
+    }
+    if (un) un->tok = off;
+    off = align_up(off + (size_t)B * s.Pu * s.d * 2);
   }
   return off;
 }
@@ -136,10 +156,11 @@ AppendWs append_ws(const Shape& s, int B, int m) {
 }
 
 struct ScoreWs { size_t qn, kn, vn, xn, ss, hid, total; };
-ScoreWs score_ws(const Shape& s, int C) {
+// C groups of Pn NS rows
+ScoreWs score_ws(const Shape& s, int C, int Pn) {
   ScoreWs w;
   size_t off = 0;
-  const size_t rows = (size_t)C * s.P;
+  const size_t rows = (size_t)C * Pn;
   w.qn = off; off = align_up(off + rows * s.d * 2);
   w.kn = off; off = align_up(off + rows * s.d * 2);
   w.vn = off; off = align_up(off + rows * s.d * 2);
@@ -149,6 +170,16 @@ ScoreWs score_ws(const Shape& s, int C) {
   w.total = off;
   return w;
 }
+
+// The user-side NS pass of one user (C = 1, Pu rows) plus its fp32 output rows, run in a
+// workspace after the S side has finished with it.
+size_t user_pass_ws(const Shape& s) {
+  if (s.Pu == 0) return 0;
+  return score_ws(s, 1, s.Pu).total + align_up((size_t)s.Pu * s.d * 4);
+}
+
+size_t prefill_need(const Shape& s, int B) { return std::max(prefill_ws(s, B).total, user_pass_ws(s)); }
+size_t append_need(const Shape& s, int B, int m) { return std::max(append_ws(s, B, m).total, user_pass_ws(s)); }
 
 GemmParams base_gemm(const Shape& s) {
   GemmParams g;
@@ -300,41 +331,57 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
   return ONETRANS_OK;
 }
 
+// One pass of NS rows through every layer: C groups of Pn rows, the NS positions
+// p0..p0+Pn-1 of the sequence (private parameters of those positions).
+//   - candidate pass (p0 = Pu): the rows also see the user's cached NS rows, uk / uv
+//     (per layer, [H][Pu][dh] of this user);
+//   - user pass (p0 = 0, Pn = Pu, C = 1): the rows' K/V of each layer go to uk / uv.
+struct NsPass {
+  int p0 = 0, Pn = 0;
+  bool user_pass = false;
+  __bf16* uk[ONETRANS_MAX_LAYERS] = {};
+  __bf16* uv[ONETRANS_MAX_LAYERS] = {};
+};
+
 // kv_ready (may be NULL): per layer, an event after which that layer's cache K/V is
 // complete; the NS attention of the layer waits for it.
 int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const char* cache_buf, const size_t* k_off,
-               const size_t* v_off, int n_users, int n_appended, int user, const uint16_t* ns_tokens, int C,
+               const size_t* v_off, int n_appended, int user, const NsPass& ps, const uint16_t* ns_tokens, int C,
                float* ns_out, char* ws, hipStream_t st, const hipEvent_t* kv_ready = nullptr) {
-  if (C == 0) return ONETRANS_OK;
-  const ScoreWs w = score_ws(s, C);
+  if (C == 0 || ps.Pn == 0) return ONETRANS_OK;
+  const int Pn = ps.Pn, p0 = ps.p0;
+  const ScoreWs w = score_ws(s, C, Pn);
   __bf16* qn = (__bf16*)(ws + w.qn);
-  __bf16* kn = (__bf16*)(ws + w.kn);
-  __bf16* vn = (__bf16*)(ws + w.vn);
   _Float16* xn = (_Float16*)(ws + w.xn);
   float* ss = (float*)(ws + w.ss);
   _Float16* hid = (_Float16*)(ws + w.hid);
-  const long d = s.d, P = s.P, rows = (long)C * P;
+  const long d = s.d, rows = (long)C * Pn;
+  const size_t nsb = s.fp8 ? 1 : 2;  // bytes per packed NS weight
   const int* vf = (const int*)cache_buf;
   {
     InputParams ip;
     memset(&ip, 0, sizeof(ip));
-    ip.tok = ns_tokens; ip.n_rows = (int)rows; ip.rows_per_seg = (int)rows; ip.d = s.d; ip.P = s.P;
+    ip.tok = ns_tokens; ip.n_rows = (int)rows; ip.rows_per_seg = (int)rows; ip.d = s.d; ip.P = Pn;
     ip.x = ns_out;
-    ip.nout = norm_out(s, xn, (const float*)(pk + lo[0].ns_ga), d, ss);
+    ip.nout = norm_out(s, xn, (const float*)(pk + lo[0].ns_ga) + p0 * d, d, ss);
     FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
     OT_HIP(launch_input_rows(ip, st), "NS input conversion launch");
   }
-  const RowMap rm{C, s.P, 0, 0, P * d, d};
+  const RowMap rm{C, Pn, 0, 0, Pn * d, d};
   for (int l = 0; l < s.L; ++l) {
     const long cap = s.cap[l];
     const int len = s.n[l] + n_appended;
+    // this pass's own K / V rows: the workspace, or the user's cache rows in the user pass
+    __bf16* kn = ps.user_pass ? ps.uk[l] : (__bf16*)(ws + w.kn);
+    __bf16* vn = ps.user_pass ? ps.uv[l] : (__bf16*)(ws + w.vn);
+    const float* scales = (const float*)(pk + lo[l].ns_scale) + p0 * 5;
     GemmParams g = base_gemm(s);
-    g.M = C; g.N = 3 * s.d; g.K = s.d; g.groups = s.P;
+    g.M = C; g.N = 3 * s.d; g.K = s.d; g.groups = Pn;
     g.rm = rm;
     g.a_in = xn;
     g.ss_in = ss; g.ss_parts = l == 0 ? 1 : s.d / 32;
-    g.w = pk + lo[l].ns_wqkv; g.w_group_stride = 3 * d * d;
-    g.wscale = (const float*)(pk + lo[l].ns_scale); g.scale_idx0 = 0; g.scale_col_div = s.d;
+    g.w = pk + lo[l].ns_wqkv + p0 * 3 * d * d * nsb; g.w_group_stride = 3 * d * d;
+    g.wscale = scales; g.scale_idx0 = 0; g.scale_col_div = s.d;
     g.q = qn; g.q_seg_stride = 0; g.q_head_stride = rows * s.dh; g.q_from = 0;
     g.k = kn; g.vt = nullptr; g.v = vn; g.kv_seg_stride = 0; g.kv_head_stride = rows * s.dh; g.kv_cap = (int)rows;
     g.kv_slot_base = 0;
@@ -354,9 +401,12 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     at.kv_seg_stride = 0; at.kv_head_stride = cap * s.dh; at.kv_cap = (int)cap;
     at.n_keys = len; at.key_pos0 = s.s_len - s.n[l]; at.q_pos0 = 0;
     at.valid_from = vf + user;
-    at.kn = kn; at.vn = vn; at.kn_head_stride = rows * s.dh; at.P = s.P;
+    at.kn = kn; at.vn = vn; at.kn_head_stride = rows * s.dh; at.P = Pn;
+    if (!ps.user_pass && p0 > 0) {
+      at.xk = ps.uk[l]; at.xv = ps.uv[l]; at.x_head_stride = (long)p0 * s.dh; at.n_x = p0;
+    }
     at.scale_log2 = scale_log2(s);
-    at.nout = norm_out(s, xn, (const float*)(pk + lo[l].ns_gf), d, ss);
+    at.nout = norm_out(s, xn, (const float*)(pk + lo[l].ns_gf) + p0 * d, d, ss);
     if (kv_ready) OT_HIP(hipStreamWaitEvent(st, kv_ready[l], 0), "layer event wait");
     {
       FamilyTimer t(ONETRANS_K_NS_ATTN, st);
@@ -364,12 +414,12 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     }
 
     GemmParams u = base_gemm(s);
-    u.M = C; u.N = s.F; u.K = s.d; u.groups = s.P;
+    u.M = C; u.N = s.F; u.K = s.d; u.groups = Pn;
     u.rm = rm;
     u.a_in = xn;
     u.ss_in = ss; u.ss_parts = s.H;
-    u.w = pk + lo[l].ns_w1; u.w_group_stride = (long)s.F * d;
-    u.wscale = (const float*)(pk + lo[l].ns_scale); u.scale_idx0 = 3;
+    u.w = pk + lo[l].ns_w1 + p0 * (size_t)s.F * d * nsb; u.w_group_stride = (long)s.F * d;
+    u.wscale = scales; u.scale_idx0 = 3;
     u.hid_out = hid;
     {
       FamilyTimer t(ONETRANS_K_NS_FFN_UP, st);
@@ -377,26 +427,66 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     }
 
     GemmParams dn = base_gemm(s);
-    dn.M = C; dn.N = s.d; dn.K = s.F; dn.groups = s.P;
+    dn.M = C; dn.N = s.d; dn.K = s.F; dn.groups = Pn;
     dn.rm = rm;
     dn.a_in = hid;
-    dn.w = pk + lo[l].ns_w2; dn.w_group_stride = d * s.F;
-    dn.wscale = (const float*)(pk + lo[l].ns_scale); dn.scale_idx0 = 4;
+    dn.w = pk + lo[l].ns_w2 + p0 * (size_t)d * s.F * nsb; dn.w_group_stride = d * s.F;
+    dn.wscale = scales; dn.scale_idx0 = 4;
     dn.res_out = ns_out;
-    dn.nout = norm_out(s, xn, l + 1 < s.L ? (const float*)(pk + lo[l + 1].ns_ga) : nullptr, d, ss);
+    dn.nout = norm_out(s, xn, l + 1 < s.L ? (const float*)(pk + lo[l + 1].ns_ga) + p0 * d : nullptr, d, ss);
     {
       FamilyTimer t(ONETRANS_K_NS_FFN_DOWN, st);
       OT_HIP(launch_gemm(GEMM_FFN_DOWN, s.fp8, true, dn, st), "NS FFN down launch");
     }
   }
-  (void)n_users;
   return ONETRANS_OK;
 }
 
+// The user-side NS rows of users [0, B) through every layer against their current
+// cache (n_appended events after the prefill): inputs from the cache's copy, K/V of
+// each layer into the cache, outputs to ns_user_out [B][Pu][d] when non-NULL.
+int user_ns_impl(const Shape& s, const char* pk, const LayerOffsets* lo, char* cache_buf, const size_t* k_off,
+                 const size_t* v_off, const UserNsOff& un, int B, int n_appended, float* ns_user_out, char* ws,
+                 hipStream_t st) {
+  if (s.Pu == 0) return ONETRANS_OK;
+  float* tmp_out = (float*)(ws + score_ws(s, 1, s.Pu).total);
+  const long ublk = (long)s.H * s.Pu * s.dh;
+  for (int u = 0; u < B; ++u) {
+    NsPass ps;
+    ps.p0 = 0; ps.Pn = s.Pu; ps.user_pass = true;
+    for (int l = 0; l < s.L; ++l) {
+      ps.uk[l] = (__bf16*)(cache_buf + un.k[l]) + u * ublk;
+      ps.uv[l] = (__bf16*)(cache_buf + un.v[l]) + u * ublk;
+    }
+    const uint16_t* tok = (const uint16_t*)(cache_buf + un.tok) + (long)u * s.Pu * s.d;
+    float* out = ns_user_out ? ns_user_out + (long)u * s.Pu * s.d : tmp_out;
+    int rc = score_impl(s, pk, lo, cache_buf, k_off, v_off, n_appended, u, ps, tok, 1, out, ws, st);
+    if (rc) return rc;
+  }
+  return ONETRANS_OK;
+}
+
+// The candidate pass of one user's C candidates.
+NsPass candidate_pass(const Shape& s, char* cache_buf, const UserNsOff& un, int user) {
+  NsPass ps;
+  ps.p0 = s.Pu; ps.Pn = s.Pc;
+  if (s.Pu > 0) {
+    const long ublk = (long)s.H * s.Pu * s.dh;
+    for (int l = 0; l < s.L; ++l) {
+      ps.uk[l] = (__bf16*)(cache_buf + un.k[l]) + user * ublk;
+      ps.uv[l] = (__bf16*)(cache_buf + un.v[l]) + user * ublk;
+    }
+  }
+  return ps;
+}
+
 // kv_done (may be NULL): per layer, an event recorded once that layer's cache K/V is written
+// (only without user-side NS rows). With them, the user NS inputs are copied into the
+// cache and the user pass runs after the S side.
 int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const uint16_t* s_tokens,
                  const int32_t* s_lens, int B, char* cache_buf, const size_t* k_off, const size_t* v_off,
-                 float* s_out, char* ws, hipStream_t st, const hipEvent_t* kv_done = nullptr) {
+                 const UserNsOff& un, const uint16_t* ns_user_tokens, float* s_out, float* ns_user_out, char* ws,
+                 hipStream_t st, const hipEvent_t* kv_done = nullptr) {
   const PrefillWs w = prefill_ws(s, B);
   float* x = (float*)(ws + w.x);
   float* ss = (float*)(ws + w.ss);
@@ -445,6 +535,12 @@ int prefill_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const u
     OT_HIP(launch_copy_rows_f32(x + (long)(s.s_len - qL) * s.d, (long)s.s_len * s.d, s_out, (long)qL * s.d,
                               (long)qL * s.d, B, st),
          "S output copy launch");
+  }
+  if (s.Pu > 0) {
+    OT_HIP(hipMemcpyAsync(cache_buf + un.tok, ns_user_tokens, (size_t)B * s.Pu * s.d * 2, hipMemcpyDeviceToDevice, st),
+           "user NS input copy");
+    int rc = user_ns_impl(s, pk, lo, cache_buf, k_off, v_off, un, B, 0, ns_user_out, ws, st);
+    if (rc) return rc;
   }
   return ONETRANS_OK;
 }
@@ -578,12 +674,7 @@ size_t onetrans_workspace_bytes(const onetrans_config* cfg, int32_t max_users, i
                                 int32_t max_append) {
   Shape s;
   if (make_shape(cfg, s) || max_users < 0 || max_candidates < 0 || max_append < 0) return 0;
-  size_t b = prefill_ws(s, max_users).total;
-  const size_t a = append_ws(s, max_users, max_append).total;
-  const size_t c = score_ws(s, max_candidates).total;
-  if (a > b) b = a;
-  if (c > b) b = c;
-  return b;
+  return std::max({prefill_need(s, max_users), append_need(s, max_users, max_append), score_ws(s, max_candidates, s.Pc).total});
 }
 
 size_t onetrans_block_forward_workspace_bytes(const onetrans_config* cfg, int32_t B, int32_t C) {
@@ -591,29 +682,34 @@ size_t onetrans_block_forward_workspace_bytes(const onetrans_config* cfg, int32_
   if (make_shape(cfg, s) || B < 1 || C < 0) return 0;
   // the cache, then the prefill's and the scoring's workspaces side by side (they run
   // concurrently)
-  return cache_layout(s, B, nullptr, nullptr) + prefill_ws(s, B).total + score_ws(s, C).total;
+  return cache_layout(s, B, nullptr, nullptr) + prefill_need(s, B) + score_ws(s, C, s.Pc).total;
 }
 
 int onetrans_user_prefill(const onetrans_config* cfg, const void* packed, const uint16_t* s_tokens,
-                          const int32_t* s_lens, int32_t B, onetrans_kv_cache* cache, float* s_out, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+                          const int32_t* s_lens, int32_t B, const uint16_t* ns_user_tokens, onetrans_kv_cache* cache,
+                          float* s_out, float* ns_user_out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   Shape s;
   int rc = make_shape(cfg, s);
   if (rc) return rc;
   if (!packed || !s_tokens || !s_lens || !cache || !cache->buf || !s_out || !workspace)
     return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
-  if (!aligned16(packed) || !aligned16(s_tokens) || !aligned16(s_out) || !aligned16(workspace))
+  if ((s.Pu > 0) != (ns_user_tokens != nullptr))
+    return fail(ONETRANS_ERR_INVALID_ARG, "ns_user_tokens must be given exactly when n_ns_user > 0");
+  if (!aligned16(packed) || !aligned16(s_tokens) || !aligned16(s_out) || !aligned16(workspace) ||
+      !aligned16(ns_user_tokens) || !aligned16(ns_user_out))
     return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
   if (B < 1 || B > cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "B must be in [1, cache->n_users]");
   if (cache->bytes < cache_layout(s, cache->n_users, nullptr, nullptr))
     return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
-  if (workspace_bytes < prefill_ws(s, B).total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for prefill");
+  if (workspace_bytes < prefill_need(s, B)) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for prefill");
   LayerOffsets lo[ONETRANS_MAX_LAYERS];
   packed_layout(s, lo);
   size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
-  cache_layout(s, cache->n_users, k_off, v_off);
-  rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, (char*)cache->buf, k_off, v_off, s_out,
-                    (char*)workspace, stream);
+  UserNsOff un;
+  cache_layout(s, cache->n_users, k_off, v_off, &un);
+  rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, (char*)cache->buf, k_off, v_off, un,
+                    ns_user_tokens, s_out, ns_user_out, (char*)workspace, stream);
   if (rc) return rc;
   cache->n_appended = 0;
   cache->prefilled = 1;
@@ -638,11 +734,12 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
   if (cache->bytes < cache_layout(s, B, nullptr, nullptr))
     return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
   const AppendWs w = append_ws(s, B, m);
-  if (workspace_bytes < w.total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for append");
+  if (workspace_bytes < append_need(s, B, m)) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for append");
   LayerOffsets lo[ONETRANS_MAX_LAYERS];
   packed_layout(s, lo);
   size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
-  cache_layout(s, B, k_off, v_off);
+  UserNsOff un;
+  cache_layout(s, B, k_off, v_off, &un);
   char* cb = (char*)cache->buf;
   char* ws = (char*)workspace;
   _Float16* xn = (_Float16*)(ws + w.xn);
@@ -672,7 +769,8 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
     if (rc) return rc;
   }
   cache->n_appended += m;
-  return ONETRANS_OK;
+  // the user-side NS rows see the grown history: recompute them from the kept inputs
+  return user_ns_impl(s, (const char*)packed, lo, cb, k_off, v_off, un, B, cache->n_appended, nullptr, ws, stream);
 }
 
 int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, const onetrans_kv_cache* cache,
@@ -689,42 +787,60 @@ int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, co
   if (!ns_tokens || !ns_out || !workspace) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
   if (!aligned16(packed) || !aligned16(ns_tokens) || !aligned16(ns_out) || !aligned16(workspace))
     return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
-  if ((long)C * s.P > (1L << 26)) return fail(ONETRANS_ERR_UNSUPPORTED, "C * n_ns must be <= 2^26");
+  if ((long)C * s.Pc > (1L << 26)) return fail(ONETRANS_ERR_UNSUPPORTED, "C * (n_ns - n_ns_user) must be <= 2^26");
   if (cache->bytes < cache_layout(s, cache->n_users, nullptr, nullptr))
     return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
-  if (workspace_bytes < score_ws(s, C).total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for scoring");
+  if (workspace_bytes < score_ws(s, C, s.Pc).total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for scoring");
   LayerOffsets lo[ONETRANS_MAX_LAYERS];
   packed_layout(s, lo);
   size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
-  cache_layout(s, cache->n_users, k_off, v_off);
-  return score_impl(s, (const char*)packed, lo, (const char*)cache->buf, k_off, v_off, cache->n_users,
-                    cache->n_appended, user, ns_tokens, C, ns_out, (char*)workspace, stream);
+  UserNsOff un;
+  cache_layout(s, cache->n_users, k_off, v_off, &un);
+  char* cb = (char*)cache->buf;
+  return score_impl(s, (const char*)packed, lo, cb, k_off, v_off, cache->n_appended, user,
+                    candidate_pass(s, cb, un, user), ns_tokens, C, ns_out, (char*)workspace, stream);
 }
 
 int onetrans_block_forward(const onetrans_config* cfg, const void* packed, const uint16_t* s_tokens,
-                           const int32_t* s_lens, int32_t B, const uint16_t* ns_tokens, int32_t C, float* s_out,
-                           float* ns_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                           const int32_t* s_lens, int32_t B, const uint16_t* ns_user_tokens, const uint16_t* ns_tokens,
+                           int32_t C, float* s_out, float* ns_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   Shape s;
   int rc = make_shape(cfg, s);
   if (rc) return rc;
-  if (!packed || !s_tokens || !s_lens || !s_out || !workspace || (C > 0 && (!ns_tokens || !ns_out)))
+  const bool cand = C > 0 && s.Pc > 0;  // candidate rows to score
+  if (!packed || !s_tokens || !s_lens || !s_out || !workspace || (cand && (!ns_tokens || !ns_out)))
     return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if ((s.Pu > 0) != (ns_user_tokens != nullptr))
+    return fail(ONETRANS_ERR_INVALID_ARG, "ns_user_tokens must be given exactly when n_ns_user > 0");
   if (!aligned16(packed) || !aligned16(s_tokens) || !aligned16(s_out) || !aligned16(workspace) ||
-      (C > 0 && (!aligned16(ns_tokens) || !aligned16(ns_out))))
+      !aligned16(ns_user_tokens) || (cand && (!aligned16(ns_tokens) || !aligned16(ns_out))))
     return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
   if (B < 1 || C < 0) return fail(ONETRANS_ERR_INVALID_ARG, "B must be >= 1 and C >= 0");
-  if ((long)C * s.P > (1L << 26)) return fail(ONETRANS_ERR_UNSUPPORTED, "C * n_ns must be <= 2^26");
+  if ((long)C * s.Pc > (1L << 26)) return fail(ONETRANS_ERR_UNSUPPORTED, "C * (n_ns - n_ns_user) must be <= 2^26");
   if (workspace_bytes < onetrans_block_forward_workspace_bytes(cfg, B, C))
     return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for block_forward");
   LayerOffsets lo[ONETRANS_MAX_LAYERS];
   packed_layout(s, lo);
   size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
-  const size_t cache_bytes = cache_layout(s, B, k_off, v_off);
+  UserNsOff un;
+  const size_t cache_bytes = cache_layout(s, B, k_off, v_off, &un);
   char* cb = (char*)workspace;
   char* pws = cb + cache_bytes;
-  char* sws = pws + prefill_ws(s, B).total;
-  if (C == 0)
-    return prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, cb, k_off, v_off, s_out, pws, stream);
+  char* sws = pws + prefill_need(s, B);
+  const long per_user = (long)C * s.Pc * s.d;
+  if (!cand || s.Pu > 0) {
+    // everything on `stream`: the whole user side, then each user's candidates
+    rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, cb, k_off, v_off, un, ns_user_tokens, s_out,
+                      nullptr, pws, stream);
+    if (rc || !cand) return rc;
+    for (int u = 0; u < B; ++u) {
+      rc = score_impl(s, (const char*)packed, lo, cb, k_off, v_off, 0, u, candidate_pass(s, cb, un, u),
+                      ns_tokens + u * per_user, C, ns_out + u * per_user, sws, stream);
+      if (rc) return rc;
+    }
+    return ONETRANS_OK;
+  }
   // The S side runs on `stream`; the NS side on this thread's second stream, which starts
   // after everything queued on `stream` so far and whose layer l waits only for the
   // event after the S side's layer-l QKV (the cache rows it reads). The NS side's small
@@ -734,13 +850,12 @@ int onetrans_block_forward(const onetrans_config* cfg, const void* packed, const
   if (rc) return rc;
   OT_HIP(hipEventRecord(side->fork, stream), "fork event record");
   OT_HIP(hipStreamWaitEvent(side->st, side->fork, 0), "fork event wait");
-  rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, cb, k_off, v_off, s_out, pws, stream,
-                    side->layer);
+  rc = prefill_impl(s, (const char*)packed, lo, s_tokens, s_lens, B, cb, k_off, v_off, un, nullptr, s_out, nullptr,
+                    pws, stream, side->layer);
   if (rc) return rc;
-  const long per_user = (long)C * s.P * s.d;
   for (int u = 0; u < B; ++u) {
-    rc = score_impl(s, (const char*)packed, lo, cb, k_off, v_off, B, 0, u, ns_tokens + u * per_user, C,
-                    ns_out + u * per_user, sws, side->st, side->layer);
+    rc = score_impl(s, (const char*)packed, lo, cb, k_off, v_off, 0, u, candidate_pass(s, cb, un, u),
+                    ns_tokens + u * per_user, C, ns_out + u * per_user, sws, side->st, side->layer);
     if (rc) return rc;
   }
   OT_HIP(hipEventRecord(side->join, side->st), "join event record");
