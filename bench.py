@@ -13,6 +13,9 @@ carries:
                 the timed steps, which carry no per-launch events
   scoring_only  candidate scoring against an already-filled cache (the serving
                 steady state the cross-request K/V sharing targets)
+  user_ns       the same user with its first 8 NS positions as user-side fields:
+                they run once in the prefill and are cached; each candidate then
+                runs its 24 item / context rows against S keys + user NS keys
   prefill_batch 64 users, lengths U{1000..1500}, prefill throughput
   append        64 new events for each of those 64 users, appended to the cache
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample
@@ -95,6 +98,13 @@ def append_flops(wl, lens, m: int) -> float:
 def score_flops_per_candidate(wl, nk) -> float:
     d, F, P = wl.d_model, wl.ffn_hidden, wl.n_ns
     return sum(2 * d * 3 * d * P + 4 * d * (P * k + P * (P + 1) / 2) + 4 * d * F * P for k in nk)
+
+
+def score_flops_user_ns(wl, nk, Pu: int) -> float:
+    """Per candidate with Pu user-side NS rows cached: its Pc = P - Pu rows see the nk
+    cached S rows, the Pu user rows and its own rows up to themselves."""
+    d, F, Pc = wl.d_model, wl.ffn_hidden, wl.n_ns - Pu
+    return sum(2 * d * 3 * d * Pc + 4 * d * (Pc * (k + Pu) + Pc * (Pc + 1) / 2) + 4 * d * F * Pc for k in nk)
 
 
 def kernel_work(wl, C: int, nk, lens=None, m: int = 0):
@@ -390,6 +400,27 @@ def main():
                                "pct_bf16_mfma_peak": round(100 * sflops / (el_s / args.steps) / 1e12 /
                                                            PEAK_TFLOPS_16BIT, 2)}
         del cache
+        # user-side NS fields: the first 8 NS positions belong to the user (one candidate's
+        # rows stand in for the user's fields), prefilled once; candidates bring 24 rows
+        Pu = 8
+        cfg3 = make_config(wl.n_layers, wl.d_model, wl.n_heads, wl.ffn_hidden, wl.n_ns, wl.s_len, wl.q_sched,
+                           rms_eps=wl.rms_eps, ns_wdtype=wl.ns_wdtype, n_ns_user=Pu)
+        m3 = OneTrans(cfg3, device_weights(raw, dev), device=dev)
+        un_d = ns_d[0, 0, :Pu].unsqueeze(0).contiguous()
+        cn_d = ns_d[0, :, Pu:].contiguous()
+        cache3 = m3.new_cache(1)
+        usteps = max(3, args.steps // 4)
+        el_up = timed(lambda: m3.user_prefill(s_d, l_d, cache3, ns_user_tokens=un_d), usteps, 1, sync)
+        out3 = torch.empty(C, wl.n_ns - Pu, wl.d_model, dtype=torch.float32, device=dev)
+        el_us = timed(lambda: m3.score_candidates(cache3, 0, cn_d, out=out3), args.steps, args.warmup, sync)
+        ufl = C * score_flops_user_ns(wl, nk, Pu)
+        out["user_ns"] = {"n_ns_user": Pu, "candidate_rows": wl.n_ns - Pu,
+                          "candidates_per_s": round(C * args.steps / el_us, 1),
+                          "ms_per_call": round(el_us / args.steps * 1e3, 4),
+                          "tflops": round(ufl / (el_us / args.steps) / 1e12, 2),
+                          "pct_bf16_mfma_peak": round(100 * ufl / (el_us / args.steps) / 1e12 / PEAK_TFLOPS_16BIT, 2),
+                          "prefill_ms_with_user_ns": round(el_up / usteps * 1e3, 4)}
+        del m3, cache3
         # prefill batch and append (64 users, lengths U{1000..1500}, then 64 new events each)
         pw = PREFILL_BATCH
         log("[bench] prefill batch / append")
