@@ -63,6 +63,29 @@ def test_score_and_append_flops(ln):
     assert bench.append_flops(WL, [ln], 6) == brute_append(WL, ln, 6)
 
 
+def brute_score_user_ns(wl, ln, Pu):
+    # a candidate's rows Pu..P-1: valid S keys + all Pu user rows + own rows up to itself
+    d, F, P = wl.d_model, wl.ffn_hidden, wl.n_ns
+    vf = wl.s_len - ln
+    present = list(range(wl.s_len))
+    tot = 0
+    for q in wl.q_sched:
+        nk = sum(1 for p in present if p >= vf)
+        rows = list(range(Pu, P))
+        pairs = sum(nk + Pu + (k - Pu) + 1 for k in rows)
+        tot += 2 * d * 3 * d * len(rows) + 4 * d * pairs + 4 * d * F * len(rows)
+        present = present[len(present) - q:]
+    return tot
+
+
+@pytest.mark.parametrize("ln,Pu", [(1500, 8), (1200, 1), (1500, 0)])
+def test_user_ns_score_flops(ln, Pu):
+    nk = bench.cache_valid_rows(ONETRANS_L, ln)
+    assert bench.score_flops_user_ns(ONETRANS_L, nk, Pu) == pytest.approx(brute_score_user_ns(ONETRANS_L, ln, Pu), rel=1e-12)
+    if Pu == 0:
+        assert bench.score_flops_user_ns(ONETRANS_L, nk, 0) == pytest.approx(bench.score_flops_per_candidate(ONETRANS_L, nk))
+
+
 def test_kernel_work_sums_to_step_flops():
     wl = ONETRANS_L
     nk = bench.cache_valid_rows(wl, 1500)
