@@ -16,6 +16,10 @@ carries:
   user_ns       the same user with its first 8 NS positions as user-side fields:
                 they run once in the prefill and are cached; each candidate then
                 runs its 24 item / context rows against S keys + user NS keys
+  multi_stage   three scoring stages with their own NS weights and token counts
+                against the same cache (retrieval 4096 x 8 NS tokens, pre-rank
+                1024 x 16, fine-rank 256 x 32), the shared-user-context path of
+                the successor system
   prefill_batch 64 users, lengths U{1000..1500}, prefill throughput
   append        64 new events for each of those 64 users, appended to the cache
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample
@@ -421,6 +425,34 @@ def main():
                           "pct_bf16_mfma_peak": round(100 * ufl / (el_us / args.steps) / 1e12 / PEAK_TFLOPS_16BIT, 2),
                           "prefill_ms_with_user_ns": round(el_up / usteps * 1e3, 4)}
         del m3, cache3
+        # multi-stage scoring on one cache: each stage packs its own NS weights (seeded per
+        # stage) next to the shared S weights and scores against the cache prefilled above
+        log("[bench] multi-stage scoring")
+        cache = model.new_cache(1)
+        model.user_prefill(s_d, l_d, cache)
+        stages = []
+        for sname, n_ns_st, c_st, seed in (("retrieval", 8, 4096, 11), ("pre_rank", 16, 1024, 12), ("fine_rank", 32, 256, 0)):
+            wl_st = wl.with_(n_ns=n_ns_st, n_candidates=c_st)
+            raw_st = [dict(lw) for lw in make_weights(wl_st, seed=seed)]
+            for lw, la in zip(raw_st, raw):
+                for k in ("s_wqkv", "s_w1", "s_w2", "s_g_attn", "s_g_ffn"):
+                    lw[k] = la[k]
+            cfg_st = make_config(wl.n_layers, wl.d_model, wl.n_heads, wl.ffn_hidden, n_ns_st, wl.s_len, wl.q_sched,
+                                 rms_eps=wl.rms_eps, ns_wdtype=wl.ns_wdtype)
+            m_st = OneTrans(cfg_st, device_weights(raw_st, dev), device=dev)
+            t_st = bf16(make_ns_tokens(wl_st, seed=seed)[0], dev)
+            o_st = torch.empty(c_st, n_ns_st, wl.d_model, dtype=torch.float32, device=dev)
+            stages.append((sname, m_st, t_st, o_st, c_st, n_ns_st, score_flops_per_candidate(wl_st, nk)))
+        msteps = max(3, args.steps // 2)
+        run_all = lambda: [st[1].score_candidates(cache, 0, st[2], out=st[3]) for st in stages]
+        el_ms = timed(run_all, msteps, 2, sync)
+        per = {}
+        for sname, m_st, t_st, o_st, c_st, n_ns_st, fl_st in stages:
+            t1 = timed(lambda: m_st.score_candidates(cache, 0, t_st, out=o_st), msteps, 2, sync) / msteps
+            per[sname] = {"candidates": c_st, "ns_tokens": n_ns_st, "ms": round(t1 * 1e3, 4),
+                          "candidates_per_s": round(c_st / t1, 1), "tflops": round(fl_st * c_st / t1 / 1e12, 2)}
+        out["multi_stage"] = {"ms_all_stages": round(el_ms / msteps * 1e3, 4), "stages": per}
+        del stages, cache
         # prefill batch and append (64 users, lengths U{1000..1500}, then 64 new events each)
         pw = PREFILL_BATCH
         log("[bench] prefill batch / append")

@@ -120,7 +120,17 @@ typedef struct onetrans_kv_cache {
   int32_t n_users;
   int32_t n_appended;   /* events appended since the prefill (same for all users) */
   int32_t prefilled;    /* 1 after onetrans_user_prefill */
+  uint64_t layout_key;  /* the user-side shape the cache was laid out for (set by init) */
 } onetrans_kv_cache;
+
+/* Multi-stage scoring on one cache (the successor system's retrieval / pre-rank /
+ * fine-rank stages; agihunt.info OneTrans-V2 summary): the cache depends only on the
+ * user-side shape (n_layers, d_model, n_heads, s_len, q_sched, append_cap,
+ * n_ns_user, rms_eps) and on the S weights. Any config that shares that shape, with
+ * its own n_ns, ns_wdtype and packed NS weights, may score against a cache another
+ * such config prefilled; every call checks layout_key and rejects a cache laid out
+ * for another user-side shape. The user-side NS rows (n_ns_user > 0) are those of
+ * the model that ran the prefill. */
 
 /* ---- sizing, packing, cache set-up (host calls) -------------------------- */
 

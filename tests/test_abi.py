@@ -193,6 +193,32 @@ def test_user_ns_rows_validation(lib):
     assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(c1), 0, F, 8, F, F, big, None) == OK
 
 
+def test_cache_layout_key_gates_other_user_side_shapes(lib):
+    # a stage config that differs only in its NS side (n_ns, weight type) may use the
+    # cache; one that differs in the user-side shape is rejected before any device work
+    F = 1 << 41
+    big = 1 << 40
+    cfg = l_cfg()
+    c = _cache(lib, cfg)
+    stage = l_cfg()
+    stage.n_ns = 8
+    stage.ns_wdtype = C.W_FP8_E4M3
+    assert lib.onetrans_score_candidates(ctypes.byref(stage), F, ctypes.byref(c), 0, F, 0, F, F, big, None) == OK
+    for field, value in (("s_len", 1499), ("append_cap", 63), ("n_ns_user", 1), ("n_heads", 12)):
+        other = l_cfg()
+        setattr(other, field, value)
+        if field == "s_len":
+            other.q_sched[0] = 1499
+        assert lib.onetrans_check_config(ctypes.byref(other)) == OK
+        assert lib.onetrans_score_candidates(ctypes.byref(other), F, ctypes.byref(c), 0, F, 0, F, F, big, None) == INVALID
+        assert lib.onetrans_kv_append(ctypes.byref(other), F, F, 1, ctypes.byref(c), F, F, big, None) == INVALID
+        assert lib.onetrans_user_prefill(ctypes.byref(other), F, F, F, 1, F if other.n_ns_user else None,
+                                         ctypes.byref(c), F, None, F, big, None) == INVALID
+    other = l_cfg()
+    other.q_sched[3] -= 1
+    assert lib.onetrans_kv_cache_read(ctypes.byref(other), ctypes.byref(c), 0, 0, 1, F, F, None) == INVALID
+
+
 def test_status_strings(lib):
     for code in range(6):
         assert lib.onetrans_status_str(code).decode()

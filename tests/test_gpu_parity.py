@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 from onetrans_inputs import (CANDIDATE_HEAVY_FP8, ONETRANS_L, ONETRANS_S, PREFILL_BATCH, TINY, Workload,
-                             make_append_tokens, make_ns_tokens, make_s_tokens)
+                             make_append_tokens, make_ns_tokens, make_s_tokens, make_weights)
 from helpers import EPS, assert_close, bf16_dev, config, device_weights, model, weights
 
 torch = pytest.importorskip("torch")
@@ -206,6 +206,37 @@ def test_user_ns_score_equals_block_forward():
     mdl.user_prefill(sd, ld, cache, ns_user_tokens=bf16_dev(un))
     for u in range(s.shape[0]):
         assert torch.equal(mdl.score_candidates(cache, u, nd[u]), ns_bf[u])
+
+
+def test_multi_stage_scoring_on_one_cache():
+    # stages with their own NS weights, NS token counts and weight types score against
+    # one prefilled cache (the successor system's retrieval / pre-rank / fine-rank
+    # stages share the user context); each matches the oracle with its own NS layers
+    from unified_transformer_recommender_onetrans_amd import OneTrans
+    wl_a, lens = SMALL["b_dh64_P32"]
+    raw_a, lay_a = weights(wl_a)
+    s_keys = ("s_wqkv", "s_w1", "s_w2", "s_g_attn", "s_g_ffn")
+    s, lens, ns_a = _inputs(wl_a, lens)
+    sd, ld = bf16_dev(s), torch.from_numpy(lens).cuda()
+    ma = OneTrans(config(wl_a), device_weights(raw_a))
+    cache = ma.new_cache(s.shape[0])
+    ma.user_prefill(sd, ld, cache)
+    for name, n_ns, wdtype, n_cand, seed in (("retrieval", 8, "bf16", 9, 1), ("pre-rank", 16, "e4m3", 4, 2),
+                                             ("fine-rank", 32, "bf16", 5, 0)):
+        wl = wl_a.with_(n_ns=n_ns, ns_wdtype=wdtype, n_candidates=n_cand)
+        raw = [dict(lw) for lw in make_weights(wl, seed=seed)]
+        for lw, la in zip(raw, raw_a):
+            for k in s_keys:
+                lw[k] = la[k]
+        lay = O.layers_from_arrays(raw)
+        m = OneTrans(config(wl), device_weights(raw))
+        toks = make_ns_tokens(wl, seed=seed)
+        got = [m.score_candidates(cache, u, bf16_dev(toks[u])) for u in range(s.shape[0])]
+        torch.cuda.synchronize()
+        for u in range(s.shape[0]):
+            oc, _ = O.prefill(lay_a, wl_a.q_sched, wl_a.n_heads, EPS, s[u], int(lens[u]))
+            assert_close(got[u].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, toks[u]), wdtype,
+                         f"{name} stage, user {u}")
 
 
 def test_zero_candidates_and_capacity_errors():

@@ -29,7 +29,7 @@ class LayerWeights(ctypes.Structure):
 
 class KVCache(ctypes.Structure):
     _fields_ = [("buf", ctypes.c_void_p), ("bytes", ctypes.c_size_t), ("n_users", ctypes.c_int32),
-                ("n_appended", ctypes.c_int32), ("prefilled", ctypes.c_int32)]
+                ("n_appended", ctypes.c_int32), ("prefilled", ctypes.c_int32), ("layout_key", ctypes.c_uint64)]
 
 
 EXPORTS = {

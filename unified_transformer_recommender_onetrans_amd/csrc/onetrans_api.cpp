@@ -68,6 +68,30 @@ int make_shape(const onetrans_config* c, Shape& s) {
   return ONETRANS_OK;
 }
 
+// Key of the user-side shape a cache is laid out for: a 64-bit FNV-1a hash of every
+// config field the cache layout (and the cached values' meaning) depends on.
+uint64_t layout_key(const onetrans_config* c) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&](uint32_t v) {
+    for (int i = 0; i < 4; ++i) {
+      h ^= (v >> (8 * i)) & 0xff;
+      h *= 1099511628211ull;
+    }
+  };
+  mix(c->n_layers); mix(c->d_model); mix(c->n_heads); mix(c->s_len); mix(c->append_cap); mix(c->n_ns_user);
+  uint32_t e;
+  memcpy(&e, &c->rms_eps, 4);
+  mix(e);
+  for (int l = 0; l < c->n_layers; ++l) mix(c->q_sched[l]);
+  return h;
+}
+
+int check_cache_key(const onetrans_config* c, const onetrans_kv_cache* cache) {
+  if (cache->layout_key != layout_key(c))
+    return fail(ONETRANS_ERR_INVALID_ARG, "cache was laid out for another user-side shape");
+  return ONETRANS_OK;
+}
+
 struct LayerOffsets {
   size_t s_wqkv, s_w1, s_w2, s_ga, s_gf, ns_wqkv, ns_w1, ns_w2, ns_scale, ns_ga, ns_gf;
 };
@@ -667,6 +691,7 @@ int onetrans_kv_cache_init(const onetrans_config* cfg, int32_t n_users, void* bu
   out->n_users = n_users;
   out->n_appended = 0;
   out->prefilled = 0;
+  out->layout_key = layout_key(cfg);
   return ONETRANS_OK;
 }
 
@@ -700,6 +725,7 @@ int onetrans_user_prefill(const onetrans_config* cfg, const void* packed, const 
       !aligned16(ns_user_tokens) || !aligned16(ns_user_out))
     return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
   if (B < 1 || B > cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "B must be in [1, cache->n_users]");
+  if ((rc = check_cache_key(cfg, cache))) return rc;
   if (cache->bytes < cache_layout(s, cache->n_users, nullptr, nullptr))
     return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
   if (workspace_bytes < prefill_need(s, B)) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for prefill");
@@ -723,6 +749,7 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
   int rc = make_shape(cfg, s);
   if (rc) return rc;
   if (!packed || !cache || !cache->buf) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if ((rc = check_cache_key(cfg, cache))) return rc;
   if (!cache->prefilled) return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
   if (m < 0) return fail(ONETRANS_ERR_INVALID_ARG, "m must be >= 0");
   if (cache->n_appended + (long)m > s.append_cap) return fail(ONETRANS_ERR_CAPACITY, "append exceeds append_cap");
@@ -780,6 +807,7 @@ int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, co
   int rc = make_shape(cfg, s);
   if (rc) return rc;
   if (!packed || !cache || !cache->buf) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if ((rc = check_cache_key(cfg, cache))) return rc;
   if (!cache->prefilled) return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
   if (user < 0 || user >= cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "user out of range");
   if (C < 0) return fail(ONETRANS_ERR_INVALID_ARG, "C must be >= 0");
@@ -869,6 +897,7 @@ int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* 
   int rc = make_shape(cfg, s);
   if (rc) return rc;
   if (!cache || !cache->buf || !k_out || !v_out) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if ((rc = check_cache_key(cfg, cache))) return rc;
   if (layer < 0 || layer >= s.L) return fail(ONETRANS_ERR_INVALID_ARG, "layer out of range");
   if (user < 0 || user >= cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "user out of range");
   if (rows < 0 || rows > s.n[layer] + cache->n_appended) return fail(ONETRANS_ERR_INVALID_ARG, "rows beyond the filled length");
