@@ -347,6 +347,28 @@ def test_candidate_heavy_fp8_full_size_sampled():
     _score_sampled(CANDIDATE_HEAVY_FP8, np.array([0, 511, 1024, 2047, 3000, 4095]))
 
 
+def test_onetrans_l_user_ns_full_size_sampled():
+    # the bench's user-side NS configuration: 8 of the 32 NS positions cached with the
+    # user (the first candidate's rows stand in for the user fields), 256 candidates of 24
+    # rows scored in the launch configuration the bench times
+    wl, Pu = ONETRANS_L, 8
+    print(f"workload {wl.name}: C={wl.n_candidates}, n_ns_user={Pu}", flush=True)
+    mdl, lay = model(wl, n_ns_user=Pu)
+    s, lens = make_s_tokens(wl)
+    ns = make_ns_tokens(wl)
+    un, cn = ns[:, 0, :Pu], np.ascontiguousarray(ns[0, :, Pu:])
+    cache = mdl.new_cache(1)
+    _, un_out = mdl.user_prefill(bf16_dev(s), torch.from_numpy(lens).cuda(), cache, ns_user_tokens=bf16_dev(un),
+                                 return_user_ns=True)
+    out = mdl.score_candidates(cache, 0, bf16_dev(cn))
+    torch.cuda.synchronize()
+    oc, _ = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[0], int(lens[0]), un[0])
+    assert_close(un_out[0].cpu().numpy(), oc.ns_out, "bf16", "user NS rows")
+    sample = np.array([0, 3, 128, 254, 255])
+    assert_close(out[sample].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, cn[sample]), "bf16",
+                 f"candidates {list(sample)}")
+
+
 def test_prefill_batch_and_append_full_size_sampled():
     wl = PREFILL_BATCH
     print(f"workload {wl.name}: B={wl.n_users} m={wl.append_m}", flush=True)
