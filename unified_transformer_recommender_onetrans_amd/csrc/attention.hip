@@ -40,9 +40,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// barrier without the release fence of __syncthreads (see gemm.hip)
+// Barrier without the release fence of __syncthreads (see gemm.hip). It first waits for
+// this wave's LDS reads to return (lgkmcnt 0): a ring slot is refilled by DMA right after
+// the barrier, and the compiler may defer a read's wait to its MFMA, past the barrier.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -562,7 +565,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     scores(0, sc);
   }
   // iteration it with tile it in slot S0 (= it % 3)
-  auto step = [&](auto S0C, int it) {
+  auto step = [&](auto S0C, int it) __attribute__((always_inline)) {
     constexpr int S0 = decltype(S0C)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
     if (it + 2 < ntiles) wait_vmcnt<PER_TILE>();  // K(it + 1) and V(it) are in
     else if (it + 1 < ntiles) wait_vmcnt<V_INSTR>();
@@ -619,13 +622,98 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
       }
     sc = sn;
   };
-  int it = 0;
-#pragma unroll 1
-  for (; it + 3 <= ntiles; it += 3) {
+  // Steady-state iteration: both DMAs issue, no key of the tile is masked. In-order issue
+  // would stall on each of the four dependent score MFMAs of the next tile, so they are
+  // interleaved with this tile's exponentials, and every fragment read of the iteration
+  // is issued up front. The exponentials use the current reference max; the rare tile
+  // that moves it recomputes them after the rescale.
+  auto step_fast = [&](auto S0C, int it) __attribute__((always_inline)) {
+    constexpr int S0 = decltype(S0C)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+    wait_vmcnt<PER_TILE>();  // K(it + 1) and V(it) are in
+    lds_barrier();
+    issue_k(it + 3, S0);
+    issue_v(it + 2, S2);
+    const char* kb = kring + S1 * K_BYTES;
+    const char* vb = vring + S0 * V_BYTES;
+    bf16x8 kf[DH / 16], vf[2 * (DH / 32)];
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) kf[s] = *(const bf16x8*)(kb + k_frag[s]);
+    float mt = sc[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sc[j]);
+    mt = fmaxf(mt, other_half(mt));
+    const float msub = st.m == -INFINITY ? 0.f : -st.m * scale;
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sn;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sn[i] = 0.f;
+    bf16x8 pb[2];
+    constexpr int EPM = 16 / (DH / 16);  // exponentials per score MFMA
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sn, 0, 0, 0);
+#pragma unroll
+      for (int e = s * EPM; e < (s + 1) * EPM; ++e) pb[e / 8][e % 8] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[e], scale, msub));
+      // the V^T fragments of this tile, one per score MFMA (the K fragment just consumed
+      // frees its registers)
+      if (s < 2 * (DH / 32)) vf[s] = *(const bf16x8*)(vb + v_frag[s / (DH / 32)][s % (DH / 32)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // keep the exponentials here, under the score MFMAs (the compiler would otherwise sink
+    // them past the branch below)
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
+    if (__builtin_amdgcn_ballot_w64(mt > st.m + tau) != 0) {
+      const bool up = mt > st.m + tau;
+      const float alpha = up ? __builtin_amdgcn_exp2f((st.m - mt) * scale) : 1.f;
+      if (up) st.m = mt;
+      st.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st.o[db][j] *= alpha;
+      const float msub2 = -st.m * scale;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[8 * c + i], scale, msub2));
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c * (DH / 32) + db], pb[c], st.o[db], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 pr = {pb[c][2 * i], pb[c][2 * i + 1]};
+        st.l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, st.l, false);
+      }
+    sc = sn;
+  };
+  // a group of three iterations from `it` (a multiple of 3) may take the steady-state form
+  // when every query of the wave is valid, the first tile needs no padding mask and the
+  // group ends at least three tiles before the last (so every DMA issues and the last,
+  // possibly partial, tile is not in it)
+  const bool all_q = full_lim == n_keys;
+  const int it_fast = key_lo > t_first ? 1 : 0;
+  // (separate loops: one loop holding both forms needs about 35 more registers)
+  auto group = [&](int it) __attribute__((always_inline)) {
     step(std::integral_constant<int, 0>{}, it);
     step(std::integral_constant<int, 1>{}, it + 1);
     step(std::integral_constant<int, 2>{}, it + 2);
+  };
+  int it = 0;
+#pragma unroll 1
+  for (; it + 3 <= ntiles && !(all_q && it >= it_fast && it + 5 < ntiles); it += 3) group(it);
+#pragma unroll 1
+  for (; all_q && it + 5 < ntiles; it += 3) {
+    step_fast(std::integral_constant<int, 0>{}, it);
+    step_fast(std::integral_constant<int, 1>{}, it + 1);
+    step_fast(std::integral_constant<int, 2>{}, it + 2);
   }
+#pragma unroll 1
+  for (; it + 3 <= ntiles; it += 3) group(it);
   if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
   if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
 

@@ -100,6 +100,10 @@ __device__ __forceinline__ void wait_tiles(int later) {
 // keep the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
+  // this wave's LDS reads have returned (lgkmcnt 0; vmcnt and expcnt unconstrained): the
+  // loaders refill the stage read last right after the barrier, and the compiler may defer
+  // a fragment read's wait to its MFMA, past the barrier
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
