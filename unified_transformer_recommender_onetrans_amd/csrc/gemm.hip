@@ -118,7 +118,8 @@ __device__ __forceinline__ int swz(int c, int r) {
 // SIDE (0 = shared S weights, 1 = private NS weights) only names the instance.
 // Waves 0-3 compute (a WM x (4/WM) grid over the tile), waves 4-7 load.
 template <int KIND, bool FP8, int SIDE, int BM, int BN, int STAGES, int WM>
-__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_m, int n_tiles_n, int n_items) {
+__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_m, int n_tiles_n, int n_items,
+                                                      int n_fast) {
   constexpr int BK = 64;
   constexpr int WN = 4 / WM;
   constexpr int TM = BM / WM, TN = BN / WN;  // one compute wave's part of the tile
@@ -151,6 +152,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
   const int cnt = per + (xcd < rem ? 1 : 0);
   const int my_items = jx < cnt ? (cnt - jx + nx - 1) / nx : 0;
   const int total_steps = my_items * nk;
+  // item w -> (M tile, N tile, group). Consecutive items share the tile of the slower index,
+  // which they then read from their XCD's L2: the N index runs fastest (n_fast) when a
+  // group's activation rows outweigh its weight rows, else the M index.
+  auto tile_of = [&](int w, int& mt, int& nt, int& g) {
+    const int r = w % (n_tiles_m * n_tiles_n);
+    g = w / (n_tiles_m * n_tiles_n);
+    if (n_fast) { nt = r % n_tiles_n; mt = r / n_tiles_n; }
+    else { mt = r % n_tiles_m; nt = r / n_tiles_m; }
+  };
 
   if (wave >= 4) {
     // ================= loader waves: the only waves that touch vmcnt for operands =================
@@ -161,7 +171,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
     auto issue = [&](int s) {
       if (iss_kt == 0) {
         const int w = ib + iss_t * nx;
-        const int mt = w % n_tiles_m, nt = (w / n_tiles_m) % n_tiles_n, g = w / (n_tiles_m * n_tiles_n);
+        int mt, nt, g;
+        tile_of(w, mt, nt, g);
         const int m0 = mt * BM, n0 = nt * BN;
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i) {
@@ -218,7 +229,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
     float4 ss_raw[MI][2];
     if (KIND != GEMM_FFN_DOWN && p.ss_in) {
       const int w = ib + t * nx;
-      const int mt = w % n_tiles_m, g = w / (n_tiles_m * n_tiles_n);
+      int mt, nt, g;
+      tile_of(w, mt, nt, g);
       const int last_chunk = p.ss_stride / 4 - 1;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
@@ -236,7 +248,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
     float4 x_pre[X_EARLY ? MI : 1][X_EARLY ? NI : 1][4];
     if constexpr (X_EARLY) {
       const int w = ib + t * nx;
-      const int mt = w % n_tiles_m, nt = (w / n_tiles_m) % n_tiles_n, g = w / (n_tiles_m * n_tiles_n);
+      int mt, nt, g;
+      tile_of(w, mt, nt, g);
       const int col = nt * BN + wn * TN + 4 * (lane >> 5);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
@@ -309,7 +322,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
     // (lane % 32) of each 32x32 block and, in registers 4q..4q+3, columns
     // 8q + 4*(lane/32) + 0..3. ----
     const int w = ib + t * nx;
-    const int mt = w % n_tiles_m, nt = (w / n_tiles_m) % n_tiles_n, g = w / (n_tiles_m * n_tiles_n);
+    int mt, nt, g;
+    tile_of(w, mt, nt, g);
     const int m0 = mt * BM, n0 = nt * BN;
     const float scale = FP8 ? p.wscale[g * 5 + p.scale_idx0 + n0 / p.scale_col_div] : 1.f;
     const int half = lane >> 5;
@@ -485,8 +499,9 @@ void launch_one(const GemmParams& p, hipStream_t s) {
   const int tm = (p.M + BM - 1) / BM, tn = p.N / BN;
   const long items = (long)tm * tn * p.groups;
   const int grid = (int)(items < 256 ? items : 256);  // one workgroup per CU
+  const int n_fast = (long)p.M > (long)p.N ? 1 : 0;  // a group's rows: activations M x K, weights N x K
   hipLaunchKernelGGL((gemm_kernel<KD, FP8, SIDE, BM, BN, stages_for<KD, BM, BN, WM, FP8>(), WM>), dim3(grid), dim3(512), 0, s,
-                     p, tm, tn, (int)items);
+                     p, tm, tn, (int)items, n_fast);
 }
 
 template <int KD, int SIDE, int BM, int BN, int WM>
