@@ -20,7 +20,8 @@ carries:
                 against the same cache (retrieval 4096 x 8 NS tokens, pre-rank
                 1024 x 16, fine-rank 256 x 32), the shared-user-context path of
                 the successor system
-  prefill_batch 64 users, lengths U{1000..1500}, prefill throughput
+  prefill_batch 64 users, lengths U{1000..1500}, prefill throughput; also the time
+                of the same prefill with 8 user-side NS fields per user
   append        64 new events for each of those 64 users, appended to the cache
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample
 Inputs are seeded synthetic data with the workloads' shapes and distributions.
@@ -485,6 +486,15 @@ def main():
                          "algorithmic_gbs": round(abytes / t_a / 1e9, 1),
                          "pct_hbm_peak": round(100 * abytes / t_a / 1e9 / PEAK_HBM_GBS, 2)}
         del m2, pcache
+        # the same 64 users with 8 user-side NS fields each: their pass runs once for the batch
+        cfg4 = make_config(pw.n_layers, pw.d_model, pw.n_heads, pw.ffn_hidden, pw.n_ns, pw.s_len, pw.q_sched,
+                           rms_eps=pw.rms_eps, n_ns_user=8)
+        m4 = OneTrans(cfg4, device_weights(raw, dev), device=dev)
+        pu_d = bf16(np.ascontiguousarray(make_ns_tokens(pw, n_users=pw.n_users, n_candidates=1)[:, 0, :8]), dev)
+        c4 = m4.new_cache(pw.n_users)
+        el_pu = timed(lambda: m4.user_prefill(ps_d, pl_d, c4, ns_user_tokens=pu_d), psteps, 1, sync)
+        out["prefill_batch"]["ms_per_call_with_8_user_ns_fields"] = round(el_pu / psteps * 1e3, 3)
+        del m4, c4
 
     if not args.no_cpu_baseline:
         log("[bench] oracle CPU baseline")

@@ -194,6 +194,24 @@ def test_user_ns_prefill_append_score_match_oracle(name):
                      f"user {u} score after append")
 
 
+def test_user_ns_batched_pass_equals_single_user_passes():
+    # the user pass of several users runs as one launch per kernel, one attention segment per
+    # user; each user's rows must come out exactly as from a prefill of that user alone
+    wl, lens, Pu = USER_NS["a_dh32_P5_u2"]
+    mdl, _ = model(wl, n_ns_user=Pu)
+    s, lens, cn, un = _user_inputs(wl, lens, Pu)
+    sd, ld, nd = _dev(s, lens, cn)
+    B = s.shape[0]
+    cache = mdl.new_cache(B)
+    _, un_all = mdl.user_prefill(sd, ld, cache, ns_user_tokens=bf16_dev(un), return_user_ns=True)
+    for u in range(B):
+        c1 = mdl.new_cache(1)
+        _, un_one = mdl.user_prefill(sd[u:u + 1].contiguous(), ld[u:u + 1].contiguous(), c1,
+                                     ns_user_tokens=bf16_dev(un[u:u + 1]), return_user_ns=True)
+        assert torch.equal(un_one[0], un_all[u]), f"user {u}"
+        assert torch.equal(mdl.score_candidates(c1, 0, nd[u]), mdl.score_candidates(cache, u, nd[u])), f"user {u}"
+
+
 def test_user_ns_score_equals_block_forward():
     # the same kernels on the same inputs: scoring against a prefilled cache reproduces
     # block_forward bit for bit, also with user-side NS rows

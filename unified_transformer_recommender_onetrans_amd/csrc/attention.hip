@@ -445,7 +445,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int qb = wave >> 1, kh = wave & 1;
-  const int h = blockIdx.y;
+  const int h = blockIdx.y, seg = blockIdx.z;
   const int wq0 = blockIdx.x * (NB * 32) + qb * 32;
   const int qi = wq0 + l32;
   const bool q_ok = qi < p.nq;
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
 
   bf16x8 qf[DH / 16];
   {
-    const __bf16* qrow = p.q + h * p.q_head_stride + (long)(q_ok ? qi : 0) * DH;
+    const __bf16* qrow = p.q + seg * p.q_seg_stride + h * p.q_head_stride + (long)(q_ok ? qi : 0) * DH;
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
       bf16x8 v = *(const bf16x8*)(qrow + s * 16 + half * 8);
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
       qf[s] = v;
     }
   }
-  const int key_lo = max(0, p.valid_from[0] - p.key_pos0);
+  const int key_lo = max(0, p.valid_from[seg] - p.key_pos0);
   const int n_keys = p.n_keys;
   const int my_lim = q_ok ? n_keys : 0;
   const int full_lim = wq0 + 31 < p.nq ? n_keys : 0;  // tiles ending at or below it need no mask
@@ -476,8 +476,8 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     for (int j = 0; j < 16; ++j) st.o[db][j] = 0.f;
 
   // ---- per-lane sources of the tile DMA (slots beyond the filled length hold zeros) ----
-  const char* kbase = (const char*)(p.k + h * p.kv_head_stride);
-  const char* vbase = (const char*)(p.vt + h * p.kv_head_stride);
+  const char* kbase = (const char*)(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride);
+  const char* vbase = (const char*)(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride);
   uint32_t k_off[K_INSTR], v_off[V_INSTR];
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
@@ -766,8 +766,8 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     const int my_first = (qi / P) * P;
 #pragma unroll 1
     for (int t0 = g_lo; t0 <= g_hi; t0 += 32)
-      key_block(p.kn + h * p.kn_head_stride, p.vn + h * p.kn_head_stride, p.nq, t0,
-                [&](int key) { return key <= qi && key >= my_first; });
+      key_block(p.kn + seg * p.kn_seg_stride + h * p.kn_head_stride, p.vn + seg * p.kn_seg_stride + h * p.kn_head_stride,
+                p.nq, t0, [&](int key) { return key <= qi && key >= my_first; });
   }
 
   // ---- merge the two key halves of each query block (LDS of the tile ring is free) ----
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   __syncthreads();
   if (kh == 1 || !q_ok) return;
   OutRow<DH> orow;
-  out_row_load<DH, true>(p, 0, h, qi, orow);
+  out_row_load<DH, true>(p, seg, h, qi, orow);
   const float m1 = mw[lane], l1 = mw[64 + lane];
   const float m = fmaxf(st.m, m1);
   const float f0 = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - m) * p.scale_log2);
@@ -796,7 +796,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) st.o[db][j] = st.o[db][j] * f0 + mw[128 + (db * 16 + j) * 64 + lane] * f1;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  out_row_store<DH, true>(p, 0, h, qi, orow, st.o, inv);
+  out_row_store<DH, true>(p, seg, h, qi, orow, st.o, inv);
 }
 
 // S-token attention with the keys of one 32-query block split over KS waves: wave w takes
@@ -942,8 +942,8 @@ __global__ void cache_clear_tail_kernel(ClearTailParams p) {
 }  // namespace
 
 template <int DH, int NB>
-void launch_attn_ns2(const AttnParams& p, hipStream_t s) {
-  dim3 grid((p.nq + NB * 32 - 1) / (NB * 32), p.H, 1);
+void launch_attn_ns2(const AttnParams& p, int n_seg, hipStream_t s) {
+  dim3 grid((p.nq + NB * 32 - 1) / (NB * 32), p.H, n_seg);
   hipLaunchKernelGGL((attn_ns2_kernel<DH, NB>), grid, dim3(NB * 128), 0, s, p);
 }
 
@@ -969,14 +969,15 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
   const long blocks32 = (long)((p.nq + 31) / 32) * p.H * n_seg;
   if (ns) {
     // NS: each tile's keys split over two waves per query block; 2 query blocks (4 waves)
-    // per workgroup when there are blocks for 512 such workgroups, else 1
-    if (n_seg != 1) return hipErrorInvalidValue;
+    // per workgroup when there are blocks for 512 such workgroups, else 1. Segments (their
+    // own cached keys each) come with no shared extra keys.
+    if (n_seg != 1 && p.n_x > 0) return hipErrorInvalidValue;
     if (dh == 64) {
-      if (blocks32 >= 2L * 512) launch_attn_ns2<64, 2>(p, s);
-      else launch_attn_ns2<64, 1>(p, s);
+      if (blocks32 >= 2L * 512) launch_attn_ns2<64, 2>(p, n_seg, s);
+      else launch_attn_ns2<64, 1>(p, n_seg, s);
     } else {
-      if (blocks32 >= 2L * 512) launch_attn_ns2<32, 2>(p, s);
-      else launch_attn_ns2<32, 1>(p, s);
+      if (blocks32 >= 2L * 512) launch_attn_ns2<32, 2>(p, n_seg, s);
+      else launch_attn_ns2<32, 1>(p, n_seg, s);
     }
   } else if (blocks32 < 2L * 512) {
     // few S query blocks: split each block's keys over four waves

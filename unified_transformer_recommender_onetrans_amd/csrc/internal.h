@@ -122,11 +122,12 @@ struct AttnParams {
   int n_keys;        // filled key slots
   int key_pos0;      // global position of key slot 0
   int q_pos0;        // global position of query 0 (S queries: causal limit)
-  const int* valid_from;   // [seg] first valid global position (NS: one value)
-  // NS only: own keys and values of the candidates, row-major kn, vn [H][nq][dh]; P NS tokens each
-  const __bf16* kn; const __bf16* vn; long kn_head_stride; int P;
-  // NS only: n_x keys every query sees in full (the user's cached NS rows), row-major
-  // xk, xv [H][n_x][dh]; n_x = 0: none
+  const int* valid_from;   // [seg] first valid global position
+  // NS only: own keys and values of the rows, row-major kn, vn [seg][H][nq][dh] (strides
+  // kn_seg_stride, kn_head_stride); P NS tokens per group of rows
+  const __bf16* kn; const __bf16* vn; long kn_seg_stride, kn_head_stride; int P;
+  // NS only, one segment: n_x keys every query sees in full (the user's cached NS rows),
+  // row-major xk, xv [H][n_x][dh]; n_x = 0: none
   const __bf16* xk; const __bf16* xv; long x_head_stride; int n_x;
   float scale_log2;  // log2(e) / sqrt(dh)
   // the FFN norm's operand: hidden row seg * nq + i, gain group i % P, partial slot h

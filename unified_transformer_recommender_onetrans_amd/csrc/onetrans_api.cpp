@@ -197,13 +197,14 @@ ScoreWs score_ws(const Shape& s, int C, int Pn) {
 
 // The user-side NS pass of one user (C = 1, Pu rows) plus its fp32 output rows, run in a
 // workspace after the S side has finished with it.
-size_t user_pass_ws(const Shape& s) {
+// the user pass of B users: its NS workspace, then room for outputs nobody asked for
+size_t user_pass_ws(const Shape& s, int B) {
   if (s.Pu == 0) return 0;
-  return score_ws(s, 1, s.Pu).total + align_up((size_t)s.Pu * s.d * 4);
+  return score_ws(s, B, s.Pu).total + align_up((size_t)B * s.Pu * s.d * 4);
 }
 
-size_t prefill_need(const Shape& s, int B) { return std::max(prefill_ws(s, B).total, user_pass_ws(s)); }
-size_t append_need(const Shape& s, int B, int m) { return std::max(append_ws(s, B, m).total, user_pass_ws(s)); }
+size_t prefill_need(const Shape& s, int B) { return std::max(prefill_ws(s, B).total, user_pass_ws(s, B)); }
+size_t append_need(const Shape& s, int B, int m) { return std::max(append_ws(s, B, m).total, user_pass_ws(s, B)); }
 
 GemmParams base_gemm(const Shape& s) {
   GemmParams g;
@@ -359,7 +360,9 @@ int run_s_layer(const Shape& s, const char* pk, const LayerOffsets& lo, const SL
 // p0..p0+Pn-1 of the sequence (private parameters of those positions).
 //   - candidate pass (p0 = Pu): the rows also see the user's cached NS rows, uk / uv
 //     (per layer, [H][Pu][dh] of this user);
-//   - user pass (p0 = 0, Pn = Pu, C = 1): the rows' K/V of each layer go to uk / uv.
+//   - user pass (p0 = 0, Pn = Pu, C = the number of users, user = 0): group c is user c's
+//     NS rows, which see that user's cached S rows (one attention segment per user); the
+//     rows' K/V of each layer go to uk / uv ([B][H][Pu][dh], users 0..C-1).
 struct NsPass {
   int p0 = 0, Pn = 0;
   bool user_pass = false;
@@ -391,7 +394,10 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     FamilyTimer t(ONETRANS_K_ELEMENTWISE, st);
     OT_HIP(launch_input_rows(ip, st), "NS input conversion launch");
   }
-  const RowMap rm{C, Pn, 0, 0, Pn * d, d};
+  // candidates: one segment of C groups; user pass: one segment per user (row c * Pn + j
+  // either way; the segment index only places K/V and picks the user's cached keys)
+  const RowMap rm = ps.user_pass ? RowMap{1, Pn, Pn * d, 0, Pn * d, d} : RowMap{C, Pn, 0, 0, Pn * d, d};
+  const int n_seg = ps.user_pass ? C : 1;
   for (int l = 0; l < s.L; ++l) {
     const long cap = s.cap[l];
     const int len = s.n[l] + n_appended;
@@ -406,9 +412,13 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     g.ss_in = ss; g.ss_parts = l == 0 ? 1 : s.d / 32;
     g.w = pk + lo[l].ns_wqkv + p0 * 3 * d * d * nsb; g.w_group_stride = 3 * d * d;
     g.wscale = scales; g.scale_idx0 = 0; g.scale_col_div = s.d;
-    g.q = qn; g.q_seg_stride = 0; g.q_head_stride = rows * s.dh; g.q_from = 0;
-    g.k = kn; g.vt = nullptr; g.v = vn; g.kv_seg_stride = 0; g.kv_head_stride = rows * s.dh; g.kv_cap = (int)rows;
-    g.kv_slot_base = 0;
+    g.q = qn; g.q_seg_stride = ps.user_pass ? Pn * s.dh : 0; g.q_head_stride = rows * s.dh; g.q_from = 0;
+    g.k = kn; g.vt = nullptr; g.v = vn; g.kv_slot_base = 0;
+    if (ps.user_pass) {  // the cache's [user][H][Pu][dh] blocks
+      g.kv_seg_stride = (long)s.H * Pn * s.dh; g.kv_head_stride = (long)Pn * s.dh; g.kv_cap = Pn;
+    } else {
+      g.kv_seg_stride = 0; g.kv_head_stride = rows * s.dh; g.kv_cap = (int)rows;
+    }
     {
       FamilyTimer t(ONETRANS_K_NS_QKV, st);
       OT_HIP(launch_gemm(GEMM_QKV, s.fp8, true, g, st), "NS QKV GEMM launch");
@@ -416,16 +426,16 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
 
     AttnParams at;
     memset(&at, 0, sizeof(at));
-    at.nq = (int)rows; at.H = s.H; at.d = s.d;
-    at.q = qn; at.q_seg_stride = 0; at.q_head_stride = rows * s.dh;
-    at.res = ns_out; at.res_seg_stride = 0; at.res_row_base = 0; at.res_row_stride = d;
+    at.nq = (int)(rows / n_seg); at.H = s.H; at.d = s.d;
+    at.q = qn; at.q_seg_stride = g.q_seg_stride; at.q_head_stride = rows * s.dh;
+    at.res = ns_out; at.res_seg_stride = ps.user_pass ? Pn * d : 0; at.res_row_base = 0; at.res_row_stride = d;
     const long user_off = (long)user * s.H * cap * s.dh;
     at.k = (const __bf16*)(cache_buf + k_off[l]) + user_off;
     at.vt = (const __bf16*)(cache_buf + v_off[l]) + user_off;
-    at.kv_seg_stride = 0; at.kv_head_stride = cap * s.dh; at.kv_cap = (int)cap;
+    at.kv_seg_stride = ps.user_pass ? (long)s.H * cap * s.dh : 0; at.kv_head_stride = cap * s.dh; at.kv_cap = (int)cap;
     at.n_keys = len; at.key_pos0 = s.s_len - s.n[l]; at.q_pos0 = 0;
     at.valid_from = vf + user;
-    at.kn = kn; at.vn = vn; at.kn_head_stride = rows * s.dh; at.P = Pn;
+    at.kn = kn; at.vn = vn; at.kn_seg_stride = g.kv_seg_stride; at.kn_head_stride = g.kv_head_stride; at.P = Pn;
     if (!ps.user_pass && p0 > 0) {
       at.xk = ps.uk[l]; at.xv = ps.uv[l]; at.x_head_stride = (long)p0 * s.dh; at.n_x = p0;
     }
@@ -434,7 +444,7 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
     if (kv_ready) OT_HIP(hipStreamWaitEvent(st, kv_ready[l], 0), "layer event wait");
     {
       FamilyTimer t(ONETRANS_K_NS_ATTN, st);
-      OT_HIP(launch_attention(true, s.dh, at, 1, st), "NS attention launch");
+      OT_HIP(launch_attention(true, s.dh, at, n_seg, st), "NS attention launch");
     }
 
     GemmParams u = base_gemm(s);
@@ -472,22 +482,16 @@ int score_impl(const Shape& s, const char* pk, const LayerOffsets* lo, const cha
 int user_ns_impl(const Shape& s, const char* pk, const LayerOffsets* lo, char* cache_buf, const size_t* k_off,
                  const size_t* v_off, const UserNsOff& un, int B, int n_appended, float* ns_user_out, char* ws,
                  hipStream_t st) {
-  if (s.Pu == 0) return ONETRANS_OK;
-  float* tmp_out = (float*)(ws + score_ws(s, 1, s.Pu).total);
-  const long ublk = (long)s.H * s.Pu * s.dh;
-  for (int u = 0; u < B; ++u) {
-    NsPass ps;
-    ps.p0 = 0; ps.Pn = s.Pu; ps.user_pass = true;
-    for (int l = 0; l < s.L; ++l) {
-      ps.uk[l] = (__bf16*)(cache_buf + un.k[l]) + u * ublk;
-      ps.uv[l] = (__bf16*)(cache_buf + un.v[l]) + u * ublk;
-    }
-    const uint16_t* tok = (const uint16_t*)(cache_buf + un.tok) + (long)u * s.Pu * s.d;
-    float* out = ns_user_out ? ns_user_out + (long)u * s.Pu * s.d : tmp_out;
-    int rc = score_impl(s, pk, lo, cache_buf, k_off, v_off, n_appended, u, ps, tok, 1, out, ws, st);
-    if (rc) return rc;
+  if (s.Pu == 0 || B == 0) return ONETRANS_OK;
+  NsPass ps;
+  ps.p0 = 0; ps.Pn = s.Pu; ps.user_pass = true;
+  for (int l = 0; l < s.L; ++l) {
+    ps.uk[l] = (__bf16*)(cache_buf + un.k[l]);
+    ps.uv[l] = (__bf16*)(cache_buf + un.v[l]);
   }
-  return ONETRANS_OK;
+  float* out = ns_user_out ? ns_user_out : (float*)(ws + score_ws(s, B, s.Pu).total);
+  return score_impl(s, pk, lo, cache_buf, k_off, v_off, n_appended, 0, ps, (const uint16_t*)(cache_buf + un.tok), B,
+                    out, ws, st);
 }
 
 // The candidate pass of one user's C candidates.
