@@ -258,7 +258,7 @@ __device__ __forceinline__ void out_row_store(const AttnParams& p, int seg, int 
   if (half == 0) no.ss[hr * no.ss_stride + h] = part;
 }
 
-template <int DH, bool NS, int NW>
+template <int DH, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   constexpr int KROW = DH * 2;                // bytes per K row (64 or 128)
   constexpr int K_BYTES = KT * KROW;
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   int my_lim = p.n_keys;   // exclusive slot bound of this lane's query
   int wave_lim = p.n_keys; // exclusive slot bound of this wave's queries
   int wave_lim_lo = p.n_keys;  // smallest bound among them: tiles below it need no upper mask
-  if (!NS) {
+  {
     const int qlast_blk = min((int)blockIdx.x * (NW * 32) + NW * 32 - 1, p.nq - 1);
     const int qlast_wave = min(wq0 + 31, p.nq - 1);
     key_hi = min(key_hi, p.q_pos0 + qlast_blk - p.key_pos0 + 1);
@@ -365,49 +365,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
     if (wave_live && t0 < wave_lim) {
       attn_tile<DH>(smem + (it % STAGES) * STAGE, t0, key_lo, my_lim, t0 < key_lo || t0 + KT > wave_lim_lo, qf, st,
                     p.scale_log2);
-    }
-  }
-
-  if (NS && wave_live) {
-    // the candidate's own NS keys: query g = c*P + k sees g' in [c*P, g];
-    // NS K and V are row-major [H][nq][dh]
-    const int P = p.P;
-    const int g_lo = (wq0 / P) * P;
-    const int g_hi = min(wq0 + 31, p.nq - 1);
-    const int my_first = (qi / P) * P;
-    const __bf16* knb = p.kn + h * p.kn_head_stride;
-    const __bf16* vnb = p.vn + h * p.kn_head_stride;
-#pragma unroll 1
-    for (int t0 = g_lo; t0 <= g_hi; t0 += 32) {
-      f32x16 sc[1];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sc[0][j] = 0.f;
-      const int krow = min(t0 + l32, p.nq - 1);
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s) {
-        const bf16x8 a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[0], 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = t0 + 8 * (j >> 2) + half * 4 + (j & 3);
-        const bool vis = q_ok && key <= qi && key >= my_first;
-        if (!vis) sc[0][j] = -INFINITY;
-      }
-      bf16x8 pb[1][2];
-      softmax_update<DH, 1>(st, sc, pb, p.scale_log2);
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int db = 0; db < DH / 32; ++db) {
-          bf16x8 a;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), p.nq - 1);
-            a[i] = vnb[(long)key * DH + db * 32 + l32];
-          }
-          st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][c], st.o[db], 0, 0, 0);
-        }
     }
   }
 
@@ -948,16 +905,11 @@ void launch_attn_ns2(const AttnParams& p, int n_seg, hipStream_t s) {
 }
 
 template <int NW>
-void launch_attn_nw(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s) {
+void launch_attn_nw(int dh, const AttnParams& p, int n_seg, hipStream_t s) {
   dim3 grid((p.nq + NW * 32 - 1) / (NW * 32), p.H, n_seg);
   dim3 block(NW * 64);
-  if (dh == 64) {
-    if (ns) hipLaunchKernelGGL((attn_kernel<64, true, NW>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_kernel<64, false, NW>), grid, block, 0, s, p);
-  } else {
-    if (ns) hipLaunchKernelGGL((attn_kernel<32, true, NW>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_kernel<32, false, NW>), grid, block, 0, s, p);
-  }
+  if (dh == 64) hipLaunchKernelGGL((attn_kernel<64, NW>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_kernel<32, NW>), grid, block, 0, s, p);
 }
 
 hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s) {
@@ -985,11 +937,11 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
     if (dh == 64) hipLaunchKernelGGL((attn_split_kernel<64, 4>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((attn_split_kernel<32, 4>), grid, dim3(256), 0, s, p);
   } else if (blocks32 >= 4L * 512) {
-    launch_attn_nw<4>(ns, dh, p, n_seg, s);
+    launch_attn_nw<4>(dh, p, n_seg, s);
   } else if (blocks32 >= 2L * 512) {
-    launch_attn_nw<2>(ns, dh, p, n_seg, s);
+    launch_attn_nw<2>(dh, p, n_seg, s);
   } else {
-    launch_attn_nw<1>(ns, dh, p, n_seg, s);
+    launch_attn_nw<1>(dh, p, n_seg, s);
   }
   return hipGetLastError();
 }
