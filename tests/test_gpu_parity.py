@@ -407,3 +407,29 @@ def test_prefill_batch_and_append_full_size_sampled():
         ok = (oc.base[l] + np.arange(oc.length(l))) >= oc.valid_from
         assert_close(k.float().cpu().numpy()[ok], oc.k[l][ok], "bf16", f"user {u} last-layer cached K")
         assert_close(v.float().cpu().numpy()[ok], oc.v[l][ok], "bf16", f"user {u} last-layer cached V")
+
+
+def test_prefill_batch_user_ns_full_size_sampled():
+    # the bench's 64-user prefill with 8 user-side NS fields per user (one attention segment
+    # per user), then an append that recomputes them; sampled users against the oracle: their
+    # user NS rows after the prefill, then two candidates scored against the grown cache
+    wl, Pu = PREFILL_BATCH, 8
+    print(f"workload {wl.name}: B={wl.n_users} n_ns_user={Pu} m={wl.append_m}", flush=True)
+    mdl, lay = model(wl, append_cap=wl.append_m, n_ns_user=Pu)
+    s, lens = make_s_tokens(wl)
+    ns = make_ns_tokens(wl, n_users=wl.n_users, n_candidates=2)
+    un = np.ascontiguousarray(ns[:, 0, :Pu])
+    cn = np.ascontiguousarray(ns[:, :, Pu:])
+    new = make_append_tokens(wl)
+    cache = mdl.new_cache(wl.n_users)
+    _, un_out = mdl.user_prefill(bf16_dev(s), torch.from_numpy(lens).cuda(), cache, ns_user_tokens=bf16_dev(un),
+                                 return_user_ns=True)
+    un_out = un_out.cpu().numpy()
+    mdl.kv_append(bf16_dev(new), cache)
+    sample = (0, int(np.argmin(lens)), 63)
+    scored = {u: mdl.score_candidates(cache, u, bf16_dev(cn[u])).cpu().numpy() for u in sample}
+    for u in sample:
+        oc, _ = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[u], int(lens[u]), un[u])
+        assert_close(un_out[u], oc.ns_out, "bf16", f"user {u} (len {lens[u]}) user NS rows")
+        oc, _ = O.append(lay, wl.n_heads, EPS, oc, new[u])
+        assert_close(scored[u], O.score(lay, wl.n_heads, EPS, oc, cn[u]), "bf16", f"user {u} candidates after append")
