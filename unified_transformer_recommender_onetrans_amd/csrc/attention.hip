@@ -761,7 +761,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
 // streaming), and the partial (max, sum, O) of the waves merge through LDS at the end.
 // Used when there are few query blocks and long key ranges (one user's prefill, appends),
 // where the plain kernel's critical path is one wave walking every key tile.
-template <int DH, int KS>
+template <int DH, int KS, bool GROUPED>
 __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   constexpr int KROW = DH * 2;
   constexpr int K_BYTES = KT * KROW;
@@ -777,8 +777,24 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int h = blockIdx.y, seg = blockIdx.z;
-  const int wq0 = blockIdx.x * 32;
+  // (query block, head, segment). GROUPED: a 1-D grid numbered so that each XCD holds a
+  // contiguous range of them (the hardware deals workgroup L to XCD L % 8): the query
+  // blocks of one (segment, head) are neighbours, run on one XCD at the same time and share
+  // its L2 copy of that head's K/V stream instead of fetching it once per block.
+  int bx, h, seg;
+  if constexpr (GROUPED) {
+    const int n_blk = (p.nq + 31) / 32;
+    const int total = gridDim.x, L = blockIdx.x;
+    const int x = L % 8, pos = x * (total / 8) + min(x, total % 8) + L / 8;
+    bx = pos % n_blk;
+    h = (pos / n_blk) % p.H;
+    seg = pos / (n_blk * p.H);
+  } else {
+    bx = blockIdx.x;
+    h = blockIdx.y;
+    seg = blockIdx.z;
+  }
+  const int wq0 = bx * 32;
   const int qi = wq0 + l32;
   const bool q_ok = qi < p.nq;
 
@@ -932,10 +948,17 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
       else launch_attn_ns2<32, 1>(p, n_seg, s);
     }
   } else if (blocks32 < 2L * 512) {
-    // few S query blocks: split each block's keys over four waves
-    dim3 grid((p.nq + 31) / 32, p.H, n_seg);
-    if (dh == 64) hipLaunchKernelGGL((attn_split_kernel<64, 4>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_split_kernel<32, 4>), grid, dim3(256), 0, s, p);
+    // few S query blocks: split each block's keys over four waves; with several segments
+    // (users), the query blocks of one (user, head) grouped on one XCD
+    if (n_seg > 1) {
+      dim3 grid((p.nq + 31) / 32 * p.H * n_seg);
+      if (dh == 64) hipLaunchKernelGGL((attn_split_kernel<64, 4, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((attn_split_kernel<32, 4, true>), grid, dim3(256), 0, s, p);
+    } else {
+      dim3 grid((p.nq + 31) / 32, p.H, n_seg);
+      if (dh == 64) hipLaunchKernelGGL((attn_split_kernel<64, 4, false>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((attn_split_kernel<32, 4, false>), grid, dim3(256), 0, s, p);
+    }
   } else if (blocks32 >= 4L * 512) {
     launch_attn_nw<4>(dh, p, n_seg, s);
   } else if (blocks32 >= 2L * 512) {
