@@ -30,6 +30,14 @@ SMALL = {
     "e_P40": (Workload(name="e", n_layers=2, d_model=192, n_heads=3, ffn_hidden=192, s_len=70,
                        q_sched=(64, 33), n_ns=40, n_users=1, n_candidates=3), [70]),
     "tiny": (TINY, [64]),
+    # key ranges of 10 tiles with every query block full: the NS attention's steady-state
+    # iterations (one and two query blocks per workgroup, dh 32 and 64) against the oracle
+    "f_dh32_long": (Workload(name="f", n_layers=2, d_model=64, n_heads=2, ffn_hidden=128, s_len=600,
+                             q_sched=(600, 300), n_ns=16, n_users=1, n_candidates=8), [600]),
+    "g_dh32_nb2": (Workload(name="g", n_layers=2, d_model=128, n_heads=4, ffn_hidden=256, s_len=520,
+                            q_sched=(520, 260), n_ns=32, n_users=1, n_candidates=256), [470]),
+    "h_dh64_long": (Workload(name="h", n_layers=2, d_model=128, n_heads=2, ffn_hidden=256, s_len=640,
+                             q_sched=(640, 320), n_ns=8, n_users=2, n_candidates=8), [640, 590]),
 }
 
 
