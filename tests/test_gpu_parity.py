@@ -441,3 +441,41 @@ def test_prefill_batch_user_ns_full_size_sampled():
         assert_close(un_out[u], oc.ns_out, "bf16", f"user {u} (len {lens[u]}) user NS rows")
         oc, _ = O.append(lay, wl.n_heads, EPS, oc, new[u])
         assert_close(scored[u], O.score(lay, wl.n_heads, EPS, oc, cn[u]), "bf16", f"user {u} candidates after append")
+
+
+def test_hip_graph_replays_match_eager():
+    # scoring and the block forward captured in a HIP graph (through torch's capture of the
+    # current stream; the block forward also forks its second stream inside the capture):
+    # every replay, with eager work and synchronisations between replays, must reproduce
+    # the eager outputs bit for bit
+    wl, lens = SMALL["b_dh64_P32"]
+    mdl, _ = model(wl)
+    s, lens, ns = _inputs(wl, lens)
+    sd, ld, nd = _dev(s, lens, ns)
+    cache = mdl.new_cache(s.shape[0])
+    mdl.user_prefill(sd, ld, cache)
+    eager_sc = mdl.score_candidates(cache, 0, nd[0]).clone()
+    eager_t, eager_n = (x.clone() for x in mdl.block_forward(sd, ld, nd))
+    torch.cuda.synchronize()
+    out_sc = torch.empty_like(eager_sc)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream, as torch's capture expects
+        mdl.score_candidates(cache, 0, nd[0], out=out_sc)
+        mdl.block_forward(sd, ld, nd)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g_sc, g_bf = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_sc):
+        mdl.score_candidates(cache, 0, nd[0], out=out_sc)
+    with torch.cuda.graph(g_bf):
+        bf_t, bf_n = mdl.block_forward(sd, ld, nd)
+    for i in range(4):
+        out_sc.fill_(float("nan"))
+        bf_n.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g_sc.replay()
+        g_bf.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_sc, eager_sc), f"scoring replay {i}"
+        assert torch.equal(bf_t, eager_t) and torch.equal(bf_n, eager_n), f"block forward replay {i}"
