@@ -11,6 +11,8 @@ carries:
                 about 6 us of pipeline drain per record, so the events run in a
                 second pass of the same number of identical steps right after
                 the timed steps, which carry no per-launch events
+  step_ms_p10_p50_p90  the spread of single steps, from events around each step of
+                a further pass (every record drains the pipeline)
   scoring_only  candidate scoring against an already-filled cache (the serving
                 steady state the cross-request K/V sharing targets)
   user_ns       the same user with its first 8 NS positions as user-side fields:
@@ -369,6 +371,17 @@ def main():
     sync()
     ms_dom, n_dom = kernel_timing_read(dominant)
     kernel_timing_enable([])
+    # the spread of single steps: the same number of steps again, each between two events
+    # on the caller's stream (a record drains the pipeline, so these are not the timed steps)
+    cur = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(cur)
+        step()
+        e1.record(cur)
+    sync()
+    per_step = np.sort([e0.elapsed_time(e1) for e0, e1 in evs])
+    pct = lambda q: round(float(np.percentile(per_step, q)), 4)
     fl, by = work[dominant]
     roof = roofline_entry(dominant, fl * args.steps, by * args.steps, ms_dom, n_dom,
                           measured_traffic(dominant, args.workload))
@@ -389,6 +402,7 @@ def main():
         "step_gflop": round(step_flops / 1e9, 2),
         "roofline": roof,
         "kernel_us_per_step": breakdown,
+        "step_ms_p10_p50_p90": [pct(10), pct(50), pct(90)],
     }
 
     if not args.no_sub:
