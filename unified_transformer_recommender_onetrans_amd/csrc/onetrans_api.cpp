@@ -195,9 +195,8 @@ ScoreWs score_ws(const Shape& s, int C, int Pn) {
   return w;
 }
 
-// The user-side NS pass of one user (C = 1, Pu rows) plus its fp32 output rows, run in a
-// workspace after the S side has finished with it.
-// the user pass of B users: its NS workspace, then room for outputs nobody asked for
+// The user-side NS pass of B users (B groups of Pu rows) plus their fp32 output rows when
+// the caller asked for none, run in a workspace after the S side has finished with it.
 size_t user_pass_ws(const Shape& s, int B) {
   if (s.Pu == 0) return 0;
   return score_ws(s, B, s.Pu).total + align_up((size_t)B * s.Pu * s.d * 4);
