@@ -293,6 +293,58 @@ def cpu_baseline(wl, raw, s, lens, ns, budget_s: float):
             "seconds": round(t2 - t0, 2)}
 
 
+def prefill_append_parts(raw, dev, steps, sync, log):
+    """The prefill batch (64 users, lengths U{1000..1500}) and the append of 64 new events
+    per user, then the same prefill with 8 user-side NS fields per user; returns the
+    "prefill_batch" and "append" entries of the JSON line."""
+    import torch
+    from unified_transformer_recommender_onetrans_amd import OneTrans, make_config
+    res = {}
+    # prefill batch and append (64 users, lengths U{1000..1500}, then 64 new events each)
+    pw = PREFILL_BATCH
+    log("[bench] prefill batch / append")
+    ps, plens = make_s_tokens(pw)
+    pnew = make_append_tokens(pw)
+    cfg2 = make_config(pw.n_layers, pw.d_model, pw.n_heads, pw.ffn_hidden, pw.n_ns, pw.s_len, pw.q_sched,
+                       append_cap=pw.append_m, rms_eps=pw.rms_eps)
+    m2 = OneTrans(cfg2, device_weights(raw, dev), device=dev)
+    ps_d, pl_d, pn_d = bf16(ps, dev), torch.from_numpy(plens).to(dev), bf16(pnew, dev)
+    pcache = m2.new_cache(pw.n_users)
+    psteps = max(3, steps // 4)
+    el_p = timed(lambda: m2.user_prefill(ps_d, pl_d, pcache), psteps, 1, sync)
+    pfl = prefill_flops(pw, plens)
+    pt = pfl / (el_p / psteps) / 1e12
+
+    def app():
+        pcache.c.n_appended = 0  # rewrite the same rows each time: identical work per call
+        m2.kv_append(pn_d, pcache)
+    el_a = timed(app, psteps, 1, sync)
+    afl = append_flops(pw, plens, pw.append_m)
+    aw = kernel_work(pw, 0, None, lens=plens, m=pw.append_m)
+    abytes = sum(b for _, b in aw.values())
+    t_a = el_a / psteps
+    res["prefill_batch"] = {"users": pw.n_users, "prefills_per_s": round(pw.n_users / (el_p / psteps), 1),
+                            "ms_per_call": round(el_p / psteps * 1e3, 3), "tflops": round(pt, 2),
+                            "pct_bf16_mfma_peak": round(100 * pt / PEAK_TFLOPS_16BIT, 2)}
+    res["append"] = {"users": pw.n_users, "events_per_user": pw.append_m,
+                     "events_per_s": round(pw.n_users * pw.append_m / t_a, 1),
+                     "ms_per_call": round(t_a * 1e3, 4), "tflops": round(afl / t_a / 1e12, 2),
+                     "algorithmic_gbs": round(abytes / t_a / 1e9, 1),
+                     "pct_hbm_peak": round(100 * abytes / t_a / 1e9 / PEAK_HBM_GBS, 2)}
+    del m2, pcache
+    # the same 64 users with 8 user-side NS fields each: their pass runs once for the batch
+    cfg4 = make_config(pw.n_layers, pw.d_model, pw.n_heads, pw.ffn_hidden, pw.n_ns, pw.s_len, pw.q_sched,
+                       rms_eps=pw.rms_eps, n_ns_user=8)
+    m4 = OneTrans(cfg4, device_weights(raw, dev), device=dev)
+    pu_d = bf16(np.ascontiguousarray(make_ns_tokens(pw, n_users=pw.n_users, n_candidates=1)[:, 0, :8]), dev)
+    c4 = m4.new_cache(pw.n_users)
+    el_pu = timed(lambda: m4.user_prefill(ps_d, pl_d, c4, ns_user_tokens=pu_d), psteps, 1, sync)
+    res["prefill_batch"]["ms_per_call_with_8_user_ns_fields"] = round(el_pu / psteps * 1e3, 3)
+    del m4, c4
+
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +354,8 @@ def main():
     ap.add_argument("--no-sub", action="store_true", help="skip the prefill-batch / append / scoring-only parts")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--workload", default="onetrans_l", choices=["onetrans_l", "onetrans_s", "candidate_heavy_fp8"])
+    ap.add_argument("--prefill-append-only", action="store_true",
+                    help="only the prefill-batch / append measurements (one JSON line of their own)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -324,6 +378,9 @@ def main():
     dev = torch.device("cuda:0")
     sync = lambda: torch.cuda.synchronize(dev)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    if args.prefill_append_only:
+        print(json.dumps(prefill_append_parts(make_weights(PREFILL_BATCH), dev, args.steps, sync, log)), flush=True)
+        return
 
     wl = {"onetrans_l": ONETRANS_L, "onetrans_s": ONETRANS_S, "candidate_heavy_fp8": CANDIDATE_HEAVY_FP8}[
         args.workload]
@@ -468,47 +525,7 @@ def main():
                           "candidates_per_s": round(c_st / t1, 1), "tflops": round(fl_st * c_st / t1 / 1e12, 2)}
         out["multi_stage"] = {"ms_all_stages": round(el_ms / msteps * 1e3, 4), "stages": per}
         del stages, cache
-        # prefill batch and append (64 users, lengths U{1000..1500}, then 64 new events each)
-        pw = PREFILL_BATCH
-        log("[bench] prefill batch / append")
-        ps, plens = make_s_tokens(pw)
-        pnew = make_append_tokens(pw)
-        cfg2 = make_config(pw.n_layers, pw.d_model, pw.n_heads, pw.ffn_hidden, pw.n_ns, pw.s_len, pw.q_sched,
-                           append_cap=pw.append_m, rms_eps=pw.rms_eps)
-        m2 = OneTrans(cfg2, device_weights(raw, dev), device=dev)
-        ps_d, pl_d, pn_d = bf16(ps, dev), torch.from_numpy(plens).to(dev), bf16(pnew, dev)
-        pcache = m2.new_cache(pw.n_users)
-        psteps = max(3, args.steps // 4)
-        el_p = timed(lambda: m2.user_prefill(ps_d, pl_d, pcache), psteps, 1, sync)
-        pfl = prefill_flops(pw, plens)
-        pt = pfl / (el_p / psteps) / 1e12
-
-        def app():
-            pcache.c.n_appended = 0  # rewrite the same rows each time: identical work per call
-            m2.kv_append(pn_d, pcache)
-        el_a = timed(app, psteps, 1, sync)
-        afl = append_flops(pw, plens, pw.append_m)
-        aw = kernel_work(pw, 0, None, lens=plens, m=pw.append_m)
-        abytes = sum(b for _, b in aw.values())
-        t_a = el_a / psteps
-        out["prefill_batch"] = {"users": pw.n_users, "prefills_per_s": round(pw.n_users / (el_p / psteps), 1),
-                                "ms_per_call": round(el_p / psteps * 1e3, 3), "tflops": round(pt, 2),
-                                "pct_bf16_mfma_peak": round(100 * pt / PEAK_TFLOPS_16BIT, 2)}
-        out["append"] = {"users": pw.n_users, "events_per_user": pw.append_m,
-                         "events_per_s": round(pw.n_users * pw.append_m / t_a, 1),
-                         "ms_per_call": round(t_a * 1e3, 4), "tflops": round(afl / t_a / 1e12, 2),
-                         "algorithmic_gbs": round(abytes / t_a / 1e9, 1),
-                         "pct_hbm_peak": round(100 * abytes / t_a / 1e9 / PEAK_HBM_GBS, 2)}
-        del m2, pcache
-        # the same 64 users with 8 user-side NS fields each: their pass runs once for the batch
-        cfg4 = make_config(pw.n_layers, pw.d_model, pw.n_heads, pw.ffn_hidden, pw.n_ns, pw.s_len, pw.q_sched,
-                           rms_eps=pw.rms_eps, n_ns_user=8)
-        m4 = OneTrans(cfg4, device_weights(raw, dev), device=dev)
-        pu_d = bf16(np.ascontiguousarray(make_ns_tokens(pw, n_users=pw.n_users, n_candidates=1)[:, 0, :8]), dev)
-        c4 = m4.new_cache(pw.n_users)
-        el_pu = timed(lambda: m4.user_prefill(ps_d, pl_d, c4, ns_user_tokens=pu_d), psteps, 1, sync)
-        out["prefill_batch"]["ms_per_call_with_8_user_ns_fields"] = round(el_pu / psteps * 1e3, 3)
-        del m4, c4
+        out.update(prefill_append_parts(raw, dev, args.steps, sync, log))
 
     if not args.no_cpu_baseline:
         log("[bench] oracle CPU baseline")
