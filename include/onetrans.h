@@ -129,8 +129,8 @@ typedef struct onetrans_kv_cache {
  * n_ns_user, rms_eps) and on the S weights. Any config that shares that shape, with
  * its own n_ns, ns_wdtype and packed NS weights, may score against a cache another
  * such config prefilled; every call checks layout_key and rejects a cache laid out
- * for another user-side shape. The user-side NS rows (n_ns_user > 0) are those of
- * the model that ran the prefill. */
+ * for another user-side shape with ONETRANS_ERR_INVALID_ARG (no launch). The
+ * user-side NS rows (n_ns_user > 0) are those of the model that ran the prefill. */
 
 /* ---- sizing, packing, cache set-up (host calls) -------------------------- */
 
