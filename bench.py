@@ -25,7 +25,15 @@ carries:
   prefill_batch 64 users, lengths U{1000..1500}, prefill throughput; also the time
                 of the same prefill with 8 user-side NS fields per user
   append        64 new events for each of those 64 users, appended to the cache
-  cpu_baseline  the fp64 oracle on the host cores on a bounded sample
+  onetrans_s, candidate_heavy_fp8
+                the OneTrans-S block forward (C = 128) and the candidate-heavy one
+                (OneTrans-L shape, C = 4096, E4M3 NS weights), each with its own
+                roofline entry for its dominant kernel family and its own oracle
+                baseline (every 8th candidate for C = 4096)
+  check         the last timed step's outputs are finite and equal, bit for bit,
+                to scoring the same candidates against a separately prefilled cache
+  cpu_baseline  the fp64 oracle on the host cores on a bounded sample (also inside
+                prefill_batch / append: every 8th user, prefills/s and appends/s)
 Inputs are seeded synthetic data with the workloads' shapes and distributions.
 """
 from __future__ import annotations
@@ -241,17 +249,19 @@ def measured_traffic(family: str, workload: str):
 
 
 def roofline_entry(family, flops, nbytes, ms, launches, traffic=None):
+    """The dominant kernel family against the MI355X peaks. The path's step is bound by the
+    matrix cores at its arithmetic intensity (the algorithmic flop / byte ratio of the whole
+    step lies above the ridge), so the entry is priced against the dense 16-bit MFMA peak;
+    the family's own algorithmic bytes give its HBM fraction beside it."""
     sec = ms / 1e3
-    intensity = flops / nbytes if nbytes else float("inf")
-    common = {"traffic": traffic, "launches": launches, "avg_launch_us": round(ms / launches * 1e3, 2),
-              "algorithmic_flops_per_launch": flops / launches, "algorithmic_bytes_per_launch": nbytes / launches}
-    if intensity >= RIDGE:
-        ach = flops / sec / 1e12
-        return {"kernel": family, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_TFLOPS_16BIT,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS_16BIT, 4), **common}
-    ach = nbytes / sec / 1e9
-    return {"kernel": family, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), **common}
+    ach = flops / sec / 1e12
+    gbs = nbytes / sec / 1e9
+    return {"kernel": family, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_TFLOPS_16BIT,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS_16BIT, 4), "traffic": traffic,
+            "launches": launches, "avg_launch_us": round(ms / launches * 1e3, 2),
+            "algorithmic_flops_per_launch": flops / launches, "algorithmic_bytes_per_launch": nbytes / launches,
+            "algorithmic_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "flop_per_byte": round(flops / nbytes, 1) if nbytes else None}
 
 
 def copy_calibration(mib: int, reps: int) -> None:
@@ -266,41 +276,73 @@ def copy_calibration(mib: int, reps: int) -> None:
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "reps": reps}))
 
 
-def cpu_baseline(wl, raw, s, lens, ns, budget_s: float):
-    """The fp64 oracle (as it stands) on the host: one user's prefill, then candidates scored in
-    chunks of 16 until about `budget_s` seconds of CPU work have been spent (or all are done)."""
-    import oracle as O
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # threadpoolctl missing: report the affinity size
-        threads = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, raw, s, lens, ns, budget_s: float, stride: int = 1):
+    """The fp64 oracle (as it stands) on the host: one user's prefill, then candidates
+    0, stride, 2*stride, ... scored in chunks of 16 until about `budget_s` seconds of CPU
+    work have been spent (or the sample is done). The rate scales the scoring time to C."""
+    import oracle as O
     lay = O.layers_from_arrays(raw)
     C = ns.shape[1]
+    sample = np.arange(0, C, stride)
     t0 = time.perf_counter()
     cache, _ = O.prefill(lay, wl.q_sched, wl.n_heads, wl.rms_eps, s[0], int(lens[0]))
     t1 = time.perf_counter()
     done = 0
-    while done < C and (done == 0 or time.perf_counter() - t0 < budget_s):
-        n = min(16, C - done)
-        O.score(lay, wl.n_heads, wl.rms_eps, cache, ns[0][done:done + n])
-        done += n
+    while done < len(sample) and (done == 0 or time.perf_counter() - t1 < budget_s):
+        idx = sample[done:done + 16]
+        O.score(lay, wl.n_heads, wl.rms_eps, cache, ns[0][idx])
+        done += len(idx)
     t2 = time.perf_counter()
     step = (t1 - t0) + (t2 - t1) * C / done
-    return {"value": round(C / step, 2), "unit": "candidates/s", "cores": threads, "kind": "oracle",
-            "sample": f"one user's prefill ({t1 - t0:.1f} s) + {done} of {C} candidates scored "
+    which = "candidates" if stride == 1 else f"every {stride}th candidate"
+    return {"value": round(C / step, 2), "unit": "candidates/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"one user's prefill ({t1 - t0:.1f} s) + {done} candidates ({which}) of {C} scored "
                       f"({t2 - t1:.1f} s); the step time scales the scoring time linearly to C={C}",
             "seconds": round(t2 - t0, 2)}
 
 
-def prefill_append_parts(raw, dev, steps, sync, log):
+def cpu_baseline_prefill_append(wl, raw, s, lens, new, budget_s: float, stride: int = 8):
+    """The oracle's prefill and append of users 0, stride, 2*stride, ... of the batch
+    until about `budget_s` seconds have been spent; rates in prefills/s and appends/s."""
+    import oracle as O
+    lay = O.layers_from_arrays(raw)
+    users = list(range(0, s.shape[0], stride))
+    t_pre = t_app = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    for u in users:
+        a = time.perf_counter()
+        cache, _ = O.prefill(lay, wl.q_sched, wl.n_heads, wl.rms_eps, s[u], int(lens[u]))
+        b = time.perf_counter()
+        O.append(lay, wl.n_heads, wl.rms_eps, cache, new[u])
+        c = time.perf_counter()
+        t_pre += b - a
+        t_app += c - b
+        done += 1
+        if c - t0 > budget_s:
+            break
+    smp = f"users {users[0]}, {users[1] if done > 1 else ''}... every {stride}th, {done} of {s.shape[0]}"
+    return ({"value": round(done / t_pre, 3), "unit": "prefills/s", "cores": _blas_threads(), "kind": "oracle",
+             "sample": f"{smp}: prefill {t_pre:.1f} s"},
+            {"value": round(done / t_app, 3), "unit": "appends/s", "cores": _blas_threads(), "kind": "oracle",
+             "sample": f"{smp}: append of {new.shape[1]} events {t_app:.1f} s"})
+
+
+def prefill_append_parts(raw, dev, steps, sync, log, cpu_budget=None):
     """The prefill batch (64 users, lengths U{1000..1500}) and the append of 64 new events
     per user, then the same prefill with 8 user-side NS fields per user; returns the
     "prefill_batch" and "append" entries of the JSON line."""
     import torch
     from unified_transformer_recommender_onetrans_amd import OneTrans, make_config
     res = {}
-    # prefill batch and append (64 users, lengths U{1000..1500}, then 64 new events each)
     pw = PREFILL_BATCH
     log("[bench] prefill batch / append")
     ps, plens = make_s_tokens(pw)
@@ -327,6 +369,7 @@ def prefill_append_parts(raw, dev, steps, sync, log):
                             "ms_per_call": round(el_p / psteps * 1e3, 3), "tflops": round(pt, 2),
                             "pct_bf16_mfma_peak": round(100 * pt / PEAK_TFLOPS_16BIT, 2)}
     res["append"] = {"users": pw.n_users, "events_per_user": pw.append_m,
+                     "appends_per_s": round(pw.n_users / t_a, 1),
                      "events_per_s": round(pw.n_users * pw.append_m / t_a, 1),
                      "ms_per_call": round(t_a * 1e3, 4), "tflops": round(afl / t_a / 1e12, 2),
                      "algorithmic_gbs": round(abytes / t_a / 1e9, 1),
@@ -341,8 +384,100 @@ def prefill_append_parts(raw, dev, steps, sync, log):
     el_pu = timed(lambda: m4.user_prefill(ps_d, pl_d, c4, ns_user_tokens=pu_d), psteps, 1, sync)
     res["prefill_batch"]["ms_per_call_with_8_user_ns_fields"] = round(el_pu / psteps * 1e3, 3)
     del m4, c4
-
+    if cpu_budget:
+        log("[bench] oracle CPU baseline: prefill batch / append")
+        res["prefill_batch"]["cpu_baseline"], res["append"]["cpu_baseline"] = cpu_baseline_prefill_append(
+            pw, raw, ps, plens, pnew, cpu_budget)
     return res
+
+
+def block_forward_part(wl, raw, dev, steps, warmup, sync, log, check=False):
+    """Timed block_forward steps of one workload (1 user prefill + C candidates scored):
+    throughput, the single-step spread and the roofline entry of the dominant kernel
+    family. Returns (entry, model, device inputs, step callable)."""
+    import torch
+    from unified_transformer_recommender_onetrans_amd import OneTrans, make_config
+    from unified_transformer_recommender_onetrans_amd._capi import (KERNEL_FAMILIES, kernel_timing_enable,
+                                                                     kernel_timing_read)
+    C = wl.n_candidates
+    s, lens = make_s_tokens(wl)
+    ns = make_ns_tokens(wl)
+    cfg = make_config(wl.n_layers, wl.d_model, wl.n_heads, wl.ffn_hidden, wl.n_ns, wl.s_len, wl.q_sched,
+                      rms_eps=wl.rms_eps, ns_wdtype=wl.ns_wdtype)
+    model = OneTrans(cfg, device_weights(raw, dev), device=dev)
+    s_d, l_d, ns_d = bf16(s, dev), torch.from_numpy(lens).to(dev), bf16(ns, dev)
+    step = lambda: model.block_forward(s_d, l_d, ns_d)
+    nk = cache_valid_rows(wl, int(lens[0]))
+    step_flops = prefill_flops(wl, lens) + C * score_flops_per_candidate(wl, nk)
+    work = kernel_work(wl, C, nk, lens=lens)
+
+    # warmup: one cold step untimed, then the rest with every family timed to find the dominant one
+    step()
+    sync()
+    kernel_timing_enable(KERNEL_FAMILIES)
+    nw = max(1, warmup)
+    for _ in range(nw):
+        step()
+    sync()
+    per_family = {f: kernel_timing_read(f) for f in KERNEL_FAMILIES}
+    events_us = {f: round(ms / nw * 1e3, 1) for f, (ms, n) in per_family.items() if n}
+    dominant = max((f for f in per_family if f in work), key=lambda f: per_family[f][0])
+
+    # timed steps (no per-launch events: each one drains the pipeline), then the same
+    # number of identical steps with the dominant family event-timed on its stream
+    log(f"[bench] {wl.name}: timing {steps} steps (dominant kernel family: {dominant})")
+    kernel_timing_enable([])
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        s_out, ns_out = step()
+    sync()
+    el = time.perf_counter() - t0
+    kernel_timing_enable([dominant])
+    for _ in range(steps):
+        step()
+    sync()
+    ms_dom, n_dom = kernel_timing_read(dominant)
+    kernel_timing_enable([])
+    # the spread of single steps: the same number of steps again, each between two events
+    # on the caller's stream (a record drains the pipeline, so these are not the timed steps)
+    cur = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(cur)
+        step()
+        e1.record(cur)
+    sync()
+    per_step = np.sort([e0.elapsed_time(e1) for e0, e1 in evs])
+    pct = lambda q: round(float(np.percentile(per_step, q)), 4)
+    fl, by = work[dominant]
+    roof = roofline_entry(dominant, fl * steps, by * steps, ms_dom, n_dom, measured_traffic(dominant, wl.name))
+    tflops = step_flops / (el / steps) / 1e12
+    entry = {
+        "candidates_per_s": round(C * steps / el, 1), "ms_per_step": round(el / steps * 1e3, 4),
+        "tflops": round(tflops, 2), "pct_bf16_mfma_peak": round(100 * tflops / PEAK_TFLOPS_16BIT, 2),
+        "step_gflop": round(step_flops / 1e9, 2), "steps": steps,
+        "workload": (f"{wl.name} block_forward: 1 user x {wl.s_len} S events (pyramid {wl.q_sched[0]}->"
+                     f"{wl.q_sched[-1]}, {wl.n_layers} layers, d={wl.d_model}, {wl.n_heads} heads), C={C} "
+                     f"candidates x {wl.n_ns} NS tokens" + (", E4M3 NS weights" if wl.ns_wdtype == "e4m3" else "")),
+        "roofline": roof,
+        # HIP events around every launch of each family during the warm-up steps: each record
+        # drains its stream (about 6 us) and the two streams overlap, so these per-family sums
+        # do not add up to the step time
+        "kernel_event_us_per_step_nonadditive": events_us,
+        "step_ms_p10_p50_p90": [pct(10), pct(50), pct(90)],
+    }
+    if check:
+        # the last timed step's outputs: finite, and equal bit for bit to scoring the same
+        # candidates against a separately prefilled cache
+        cache = model.new_cache(1)
+        tail = model.user_prefill(s_d, l_d, cache)
+        ref = model.score_candidates(cache, 0, ns_d[0])
+        sync()
+        entry["check"] = {"finite": bool(torch.isfinite(ns_out).all().item() and torch.isfinite(s_out).all().item()),
+                          "block_forward_equals_scoring": bool(torch.equal(ns_out[0], ref) and torch.equal(s_out, tail))}
+        del cache
+    return entry, model, (s, lens, ns, s_d, l_d, ns_d), nk
 
 
 def main():
@@ -351,8 +486,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sub", action="store_true", help="skip the prefill-batch / append / scoring-only parts")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="only the headline workload (no scoring-only, user-side, multi-stage, prefill batch, "
+                         "append, OneTrans-S or candidate-heavy parts)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of each oracle baseline")
     ap.add_argument("--workload", default="onetrans_l", choices=["onetrans_l", "onetrans_s", "candidate_heavy_fp8"])
     ap.add_argument("--prefill-append-only", action="store_true",
                     help="only the prefill-batch / append measurements (one JSON line of their own)")
@@ -371,15 +508,15 @@ def main():
 
     import __graft_entry__
     from unified_transformer_recommender_onetrans_amd import LIB_PATH, OneTrans, make_config
-    from unified_transformer_recommender_onetrans_amd._capi import (KERNEL_FAMILIES, kernel_timing_enable,
-                                                                     kernel_timing_read)
     if not os.path.exists(LIB_PATH):
         __graft_entry__.build()
     dev = torch.device("cuda:0")
     sync = lambda: torch.cuda.synchronize(dev)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    cpu_budget = None if args.no_cpu_baseline else args.cpu_seconds
     if args.prefill_append_only:
-        print(json.dumps(prefill_append_parts(make_weights(PREFILL_BATCH), dev, args.steps, sync, log)), flush=True)
+        print(json.dumps(prefill_append_parts(make_weights(PREFILL_BATCH), dev, args.steps, sync, log, cpu_budget)),
+              flush=True)
         return
 
     wl = {"onetrans_l": ONETRANS_L, "onetrans_s": ONETRANS_S, "candidate_heavy_fp8": CANDIDATE_HEAVY_FP8}[
@@ -387,79 +524,20 @@ def main():
     C = wl.n_candidates
     log(f"[bench] generating {wl.name} inputs")
     raw = make_weights(wl)
-    s, lens = make_s_tokens(wl)
-    ns = make_ns_tokens(wl)
-    cfg = make_config(wl.n_layers, wl.d_model, wl.n_heads, wl.ffn_hidden, wl.n_ns, wl.s_len, wl.q_sched,
-                      rms_eps=wl.rms_eps, ns_wdtype=wl.ns_wdtype)
-    model = OneTrans(cfg, device_weights(raw, dev), device=dev)
-    s_d, l_d, ns_d = bf16(s, dev), torch.from_numpy(lens).to(dev), bf16(ns, dev)
-    step = lambda: model.block_forward(s_d, l_d, ns_d)
-
-    nk = cache_valid_rows(wl, int(lens[0]))
-    step_flops = prefill_flops(wl, lens) + C * score_flops_per_candidate(wl, nk)
-    work = kernel_work(wl, C, nk, lens=lens)
-
-    # warmup: one cold step untimed, then the rest with every family timed to find the dominant one
-    log("[bench] warmup")
-    step()
-    sync()
-    kernel_timing_enable(KERNEL_FAMILIES)
-    for _ in range(max(1, args.warmup)):
-        step()
-    sync()
-    per_family = {f: kernel_timing_read(f) for f in KERNEL_FAMILIES}
-    nw = max(1, args.warmup)
-    breakdown = {f: round(ms / nw * 1e3, 1) for f, (ms, n) in per_family.items() if n}
-    dominant = max((f for f in per_family if f in work), key=lambda f: per_family[f][0])
-
-    # timed steps (no per-launch events: each one drains the pipeline), then the same
-    # number of identical steps with the dominant family event-timed on its stream
-    log(f"[bench] timing {args.steps} steps (dominant kernel family: {dominant})")
-    kernel_timing_enable([])
-    sync()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    sync()
-    el = time.perf_counter() - t0
-    kernel_timing_enable([dominant])
-    for _ in range(args.steps):
-        step()
-    sync()
-    ms_dom, n_dom = kernel_timing_read(dominant)
-    kernel_timing_enable([])
-    # the spread of single steps: the same number of steps again, each between two events
-    # on the caller's stream (a record drains the pipeline, so these are not the timed steps)
-    cur = torch.cuda.current_stream(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for e0, e1 in evs:
-        e0.record(cur)
-        step()
-        e1.record(cur)
-    sync()
-    per_step = np.sort([e0.elapsed_time(e1) for e0, e1 in evs])
-    pct = lambda q: round(float(np.percentile(per_step, q)), 4)
-    fl, by = work[dominant]
-    roof = roofline_entry(dominant, fl * args.steps, by * args.steps, ms_dom, n_dom,
-                          measured_traffic(dominant, args.workload))
-
-    ms_step = el / args.steps * 1e3
-    tflops = step_flops / (el / args.steps) / 1e12
+    head, model, (s, lens, ns, s_d, l_d, ns_d), nk = block_forward_part(wl, raw, dev, args.steps, args.warmup,
+                                                                         sync, log, check=True)
     out = {
-        "metric": METRIC, "value": round(C * args.steps / el, 1), "unit": "candidates/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "metric": METRIC, "value": head["candidates_per_s"], "unit": "candidates/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp16/bf16",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
-        "config": {"workload": f"{wl.name} block_forward: 1 user x {wl.s_len} S events (pyramid "
-                               f"{wl.q_sched[0]}->{wl.q_sched[-1]}, {wl.n_layers} layers, d={wl.d_model}, "
-                               f"{wl.n_heads} heads), C={C} candidates x {wl.n_ns} NS tokens"
-                               + (", E4M3 NS weights" if wl.ns_wdtype == "e4m3" else ""),
-                   "global_batch": C, "seq_len": wl.s_len + wl.n_ns},
-        "tflops": round(tflops, 2), "pct_bf16_mfma_peak": round(100 * tflops / PEAK_TFLOPS_16BIT, 2),
-        "step_gflop": round(step_flops / 1e9, 2),
-        "roofline": roof,
-        "kernel_us_per_step": breakdown,
-        "step_ms_p10_p50_p90": [pct(10), pct(50), pct(90)],
+        "config": {"workload": head["workload"], "global_batch": C, "seq_len": wl.s_len + wl.n_ns},
+        "tflops": head["tflops"], "pct_bf16_mfma_peak": head["pct_bf16_mfma_peak"],
+        "step_gflop": head["step_gflop"],
+        "roofline": head["roofline"],
+        "kernel_event_us_per_step_nonadditive": head["kernel_event_us_per_step_nonadditive"],
+        "step_ms_p10_p50_p90": head["step_ms_p10_p50_p90"],
+        "check": head["check"],
     }
 
     if not args.no_sub:
@@ -524,12 +602,29 @@ def main():
             per[sname] = {"candidates": c_st, "ns_tokens": n_ns_st, "ms": round(t1 * 1e3, 4),
                           "candidates_per_s": round(c_st / t1, 1), "tflops": round(fl_st * c_st / t1 / 1e12, 2)}
         out["multi_stage"] = {"ms_all_stages": round(el_ms / msteps * 1e3, 4), "stages": per}
-        del stages, cache
-        out.update(prefill_append_parts(raw, dev, args.steps, sync, log))
+        del stages, cache, model
+        out.update(prefill_append_parts(raw, dev, args.steps, sync, log, cpu_budget))
+        # the other block-forward workloads: OneTrans-S (C = 128) and the candidate-heavy
+        # E4M3 case (C = 4096), each with its own roofline entry
+        for other in (ONETRANS_S, CANDIDATE_HEAVY_FP8):
+            if other.name == wl.name:
+                continue
+            log(f"[bench] generating {other.name} inputs")
+            raw_o = make_weights(other)
+            ent, m_o, (so, lo, nso, *_), _ = block_forward_part(other, raw_o, dev, args.steps, args.warmup, sync,
+                                                                log, check=True)
+            del m_o
+            torch.cuda.empty_cache()
+            if cpu_budget:
+                log(f"[bench] oracle CPU baseline: {other.name}")
+                big = other.n_candidates >= 1024  # every 8th candidate, with twice the budget
+                ent["cpu_baseline"] = cpu_baseline(other, raw_o, so, lo, nso, cpu_budget * (2 if big else 1),
+                                                   stride=8 if big else 1)
+            out[other.name] = ent
 
-    if not args.no_cpu_baseline:
+    if cpu_budget:
         log("[bench] oracle CPU baseline")
-        out["cpu_baseline"] = cpu_baseline(wl, raw, s, lens, ns, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, raw, s, lens, ns, cpu_budget)
     print(json.dumps(out), flush=True)
 
 

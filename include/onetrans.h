@@ -43,7 +43,9 @@
  *     feeding a linear map is applied as r * ((x * g) W): the operand is
  *     x * g rounded to fp16 and the row factor r = 1/sqrt(mean(x^2) + eps)
  *     (fp32) scales the accumulator, so every |x_j g_j| of the residual
- *     stream must stay within fp16 range (65504).
+ *     stream must stay below 65504 (fp16 range); entries below 2^-14 (6.1e-5)
+ *     fall on the fp16 subnormal grid (step 2^-24), so rows whose rms is far
+ *     below 1e-3 lose relative precision in their linear maps.
  *   - Not thread-safe for concurrent calls that share a workspace or a cache;
  *     calls on distinct workspaces and caches are independent.
  *   - onetrans_last_error() returns a thread-local description of the last
@@ -119,12 +121,15 @@ typedef struct onetrans_kv_cache {
   size_t bytes;
   int32_t n_users;
   int32_t n_appended;   /* events appended since the prefill (same for all users) */
-  int32_t prefilled;    /* 1 after onetrans_user_prefill */
+  int32_t prefilled;    /* users [0, prefilled) hold a prefill (set by onetrans_user_prefill; 0 before) */
   uint64_t layout_key;  /* the user-side shape the cache was laid out for (set by init) */
 } onetrans_kv_cache;
 
-/* Multi-stage scoring on one cache (the successor system's retrieval / pre-rank /
- * fine-rank stages; agihunt.info OneTrans-V2 summary): the cache depends only on the
+/* Multi-stage scoring on one cache (the successor system, OneTrans-V2: retrieval,
+ * pre-rank and fine-rank become tasks of one model that encodes the user's behaviour
+ * once per request while each stage keeps its own candidate features; rss.com
+ * OneTrans-V2 podcast page, "Key takeaways", first item, and the welcome.ai OneTrans-V2
+ * summary, "Academic Abstract"): the cache depends only on the
  * user-side shape (n_layers, d_model, n_heads, s_len, q_sched, append_cap,
  * n_ns_user, rms_eps) and on the S weights. Any config that shares that shape, with
  * its own n_ns, ns_wdtype and packed NS weights, may score against a cache another
@@ -143,7 +148,11 @@ size_t onetrans_packed_weight_bytes(const onetrans_config* cfg);
 /* Converts the caller's per-layer weights (layers[cfg->n_layers]) into the
  * packed device buffer `packed` (bf16 weights become fp16, E4M3FN codes and
  * fp32 gains/scales are copied). Asynchronous on `stream`. The packed buffer
- * must stay alive and unchanged while compute calls use it. */
+ * must stay alive and unchanged while compute calls use it.
+ * Range: the bf16 -> fp16 conversion (round to nearest even) is exact for weights
+ * with 2^-17 <= |w| < 65536 (the largest such bf16 value is 65280) and for zero; smaller magnitudes are rounded to the
+ * fp16 subnormal grid (step 2^-24) and larger ones become infinite. The call does
+ * not inspect the values; keep weights inside that range. */
 int onetrans_pack_weights(const onetrans_config* cfg, const onetrans_layer_weights* layers,
                           void* packed, size_t packed_bytes, hipStream_t stream);
 
@@ -161,7 +170,10 @@ size_t onetrans_workspace_bytes(const onetrans_config* cfg, int32_t max_users,
 
 /* ---- compute calls (asynchronous on stream) ------------------------------ */
 
-/* User prefill: runs the S side of B users through every layer, writes each
+/* User prefill (agihunt.info OneTrans summary, pyramid / KV paragraph: the S side
+ * runs once per user; asterzephyr.xyz blog, design four: the user side, profile
+ * fields included, is computed ahead and cached).
+ * Runs the S side of B users through every layer, writes each
  * layer's K/V (all n_l input rows) into `cache` and returns the last layer's
  * S outputs; then, with n_ns_user > 0, runs each user's user-side NS rows
  * (NS positions 0..n_ns_user-1, after every S row) and caches their K/V too.
@@ -174,17 +186,20 @@ size_t onetrans_workspace_bytes(const onetrans_config* cfg, int32_t max_users,
  *   ns_user_out dev fp32 [B][n_ns_user][d]: the user NS rows after the last
  *             layer, or NULL (not returned)
  * The cache must have been initialised for at least B users; it is reset
- * (n_appended = 0, prefilled = 1). */
+ * (n_appended = 0, prefilled = B): scoring, appends and reads then accept users
+ * [0, B) only, until the next prefill. */
 int onetrans_user_prefill(const onetrans_config* cfg, const void* packed,
                           const uint16_t* s_tokens, const int32_t* s_lens, int32_t B,
                           const uint16_t* ns_user_tokens, onetrans_kv_cache* cache, float* s_out,
                           float* ns_user_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* KV append: m newly arrived events per user (for all cache->n_users users)
+/* KV append (agihunt.info OneTrans summary, pyramid / KV paragraph: sequence K/V
+ * can be appended across requests).
+ * m newly arrived events per user (for the B = cache->prefilled users)
  * enter every layer as queries at the next global positions; each sees the
  * user's valid cached rows and the new events up to itself. Their K/V rows are
  * appended in place and cache->n_appended grows by m (host-side, at enqueue).
- *   new_tokens dev bf16 [B][m][d], B = cache->n_users
+ *   new_tokens dev bf16 [B][m][d], B = cache->prefilled
  *   new_out    dev fp32 [B][m][d]: the new events' outputs after the last layer
  * With n_ns_user > 0 the user-side NS rows see the grown history, so their
  * cached K/V is recomputed from the inputs the prefill kept.
@@ -193,18 +208,22 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed,
                        const uint16_t* new_tokens, int32_t m, onetrans_kv_cache* cache,
                        float* new_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Candidate scoring: the NS side of C candidates of user `user` against that
+/* Candidate scoring (agihunt.info OneTrans summary, pyramid / KV paragraph: the NS
+ * side runs per candidate against the shared S side; block paragraph: each NS token
+ * sees the full history and the NS tokens before it).
+ * The NS side of C candidates of user `user` against that
  * user's cached user-side K/V (cross-request KV sharing). A candidate has
  * Pc = n_ns - n_ns_user rows, NS positions n_ns_user..n_ns-1.
  *   ns_tokens dev bf16 [C][Pc][d]
  *   ns_out    dev fp32 [C][Pc][d]: the candidate rows after the last layer
- * C may be 0 (no work); so may Pc. */
+ * user must be below cache->prefilled. C may be 0 (no work); so may Pc. */
 int onetrans_score_candidates(const onetrans_config* cfg, const void* packed,
                               const onetrans_kv_cache* cache, int32_t user,
                               const uint16_t* ns_tokens, int32_t C, float* ns_out,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Full pass without a persistent cache: prefill of B users into a cache held
+/* Block forward (agihunt.info OneTrans summary, block and pyramid / KV paragraphs).
+ * Full pass without a persistent cache: prefill of B users into a cache held
  * in the workspace, then scoring of each user's C candidates.
  *   s_tokens, s_lens, ns_user_tokens, s_out as in onetrans_user_prefill
  *   ns_tokens dev bf16 [B][C][Pc][d], ns_out dev fp32 [B][C][Pc][d]
@@ -229,12 +248,21 @@ int onetrans_block_forward(const onetrans_config* cfg, const void* packed,
 const char* onetrans_status_str(int status);
 const char* onetrans_last_error(void);
 
-/* Copies layer `layer`'s cached K and V rows [0, rows) of user `user` into
- * k_out and v_out (dev bf16 [rows][d] each, heads concatenated along d), for
- * inspection and tests. rows must not exceed the layer's filled length. */
+/* Copies layer `layer`'s cached K and V rows [0, rows) of user `user` (below
+ * cache->prefilled) into k_out and v_out (dev bf16 [rows][d] each, heads
+ * concatenated along d), for inspection and tests. rows must not exceed the
+ * layer's filled length. */
 int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* cache, int32_t layer,
                            int32_t user, int32_t rows, uint16_t* k_out, uint16_t* v_out,
                            hipStream_t stream);
+
+/* The attention kernel instance a launch of n_queries queries per (segment, head)
+ * runs on (ns: 1 for NS queries against a cache, 0 for S queries; n_seg: users in
+ * one launch), as a static string such as "attn_kernel<64,4>", or "none" for
+ * arguments no launch takes. Pure host logic, for tests that check which
+ * instances a workload reaches. */
+const char* onetrans_attention_route(int32_t ns, int32_t head_dim, int32_t n_queries, int32_t n_heads,
+                                     int32_t n_seg);
 
 /* Kernel timing (diagnostics). While a family's bit is set in `mask`
  * (bit k = 1 << onetrans_kernel_family k), each launch of that family is

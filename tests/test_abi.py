@@ -142,8 +142,14 @@ def test_compute_calls_reject_bad_arguments(lib):
     assert lib.onetrans_kv_append(ctypes.byref(cfg), F, F, 0, ctypes.byref(c), F, F, big, None) == OK  # no-op
     cu = _cache(lib, cfg, prefilled=0)
     assert lib.onetrans_kv_append(ctypes.byref(cfg), F, F, 1, ctypes.byref(cu), F, F, big, None) == INVALID
-    # score
+    # score: only prefilled users (c holds 2 users, 1 prefilled)
     assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(c), 2, F, 8, F, F, big, None) == INVALID
+    assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(c), 1, F, 8, F, F, big, None) == INVALID
+    assert "not prefilled" in lib.onetrans_last_error().decode()
+    assert lib.onetrans_kv_cache_read(ctypes.byref(cfg), ctypes.byref(c), 0, 1, 1, F, F, None) == INVALID
+    cbad = _cache(lib, cfg, prefilled=3)  # a struct that claims more prefilled users than it holds
+    assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(cbad), 0, F, 8, F, F, big, None) == INVALID
+    assert lib.onetrans_kv_append(ctypes.byref(cfg), F, F, 1, ctypes.byref(cbad), F, F, big, None) == INVALID
     assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(c), -1, F, 8, F, F, big, None) == INVALID
     assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(cu), 0, F, 8, F, F, big, None) == INVALID
     assert lib.onetrans_score_candidates(ctypes.byref(cfg), F, ctypes.byref(c), 0, F, 8, F, F, 100, None) == WORKSPACE

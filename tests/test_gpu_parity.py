@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 from onetrans_inputs import (CANDIDATE_HEAVY_FP8, ONETRANS_L, ONETRANS_S, PREFILL_BATCH, TINY, Workload,
-                             make_append_tokens, make_ns_tokens, make_s_tokens, make_weights)
+                             bf16_round, make_append_tokens, make_ns_tokens, make_s_tokens, make_weights)
 from helpers import EPS, assert_close, bf16_dev, config, device_weights, model, weights
 
 torch = pytest.importorskip("torch")
@@ -39,6 +39,22 @@ SMALL = {
     "h_dh64_long": (Workload(name="h", n_layers=2, d_model=128, n_heads=2, ffn_hidden=256, s_len=640,
                              q_sched=(640, 320), n_ns=8, n_users=2, n_candidates=8), [640, 590]),
 }
+
+
+# many users' prefill in one launch: the S attention's tile instances with four and two
+# query blocks per workgroup (dh 32: 2048 and 1024 query blocks; dh 64: 1536), ragged
+# right-aligned histories from a single event to the full length
+MANY_USERS = {
+    "i_dh32_16users": Workload(name="i", n_layers=2, d_model=64, n_heads=2, ffn_hidden=128, s_len=2048,
+                               q_sched=(2048, 1024), n_ns=4, n_users=16, n_candidates=3),
+    "j_dh64_12users": Workload(name="j", n_layers=2, d_model=128, n_heads=2, ffn_hidden=256, s_len=2048,
+                               q_sched=(2048, 1000), n_ns=4, n_users=12, n_candidates=3),
+}
+
+
+def _many_lens(wl):
+    base = [wl.s_len, 1, 1500, wl.s_len - 1, 33, 1024, 2000, 64, 65, 1999, 700, 1, 1200, 1800, 5, 2048]
+    return [min(x, wl.s_len) for x in base[:wl.n_users]]
 
 
 def _inputs(wl, lens):
@@ -104,6 +120,32 @@ def test_prefill_append_score_match_oracle(name):
             ok = (oc.base[l] + np.arange(rows)) >= oc.valid_from
             assert_close(k.float().cpu().numpy()[ok], oc.k[l][ok], "bf16", f"user {u} layer {l} cached K")
             assert_close(v.float().cpu().numpy()[ok], oc.v[l][ok], "bf16", f"user {u} layer {l} cached V")
+
+
+@pytest.mark.parametrize("name", list(MANY_USERS))
+def test_many_user_prefill_tile_kernels(name):
+    wl = MANY_USERS[name]
+    print(f"case {name}: B={wl.n_users}", flush=True)
+    m = 7
+    mdl, lay = model(wl, append_cap=m)
+    s, lens, ns = _inputs(wl, _many_lens(wl))
+    sd, ld, nd = _dev(s, lens, ns)
+    B = s.shape[0]
+    cache = mdl.new_cache(B)
+    s_out = mdl.user_prefill(sd, ld, cache)
+    new = make_append_tokens(wl, m=m)
+    app = mdl.kv_append(bf16_dev(new), cache)
+    scored = {u: mdl.score_candidates(cache, u, nd[u]) for u in (0, 1, B - 1)}
+    torch.cuda.synchronize()
+    s_out, app = s_out.cpu().numpy(), app.cpu().numpy()
+    for u in range(B):
+        oc, ot = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[u], int(lens[u]))
+        assert_close(s_out[u], ot, wl.ns_wdtype, f"user {u} (len {lens[u]}) S tail")
+        oc, oa = O.append(lay, wl.n_heads, EPS, oc, new[u])
+        assert_close(app[u], oa, wl.ns_wdtype, f"user {u} appended rows")
+        if u in scored:
+            assert_close(scored[u].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, ns[u]), wl.ns_wdtype,
+                         f"user {u} scores after the append")
 
 
 def test_peaked_attention_moves_softmax_reference():
@@ -356,9 +398,13 @@ def _score_sampled(wl, sample):
     torch.cuda.synchronize()
     oc, ot = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[0], int(lens[0]))
     assert_close(tail[0].cpu().numpy(), ot, "bf16", "S tail")
-    ref = O.score(lay, wl.n_heads, EPS, oc, ns[0][sample])
-    assert_close(out[sample].cpu().numpy(), ref, wl.ns_wdtype, f"candidates {list(sample)}")
-    return out
+    got = out[sample].cpu().numpy()
+    ref = np.empty_like(got, dtype=np.float64)
+    for i in range(0, len(sample), 64):  # the oracle in chunks, with progress lines
+        ref[i:i + 64] = O.score(lay, wl.n_heads, EPS, oc, ns[0][sample[i:i + 64]])
+        print(f"    oracle: {min(i + 64, len(sample))} of {len(sample)} sampled candidates", flush=True)
+    assert_close(got, ref, wl.ns_wdtype, f"{len(sample)} sampled candidates")
+    return out, cache, mdl, lay, s, lens, ns
 
 
 def test_onetrans_s_full_size_sampled():
@@ -369,8 +415,53 @@ def test_onetrans_l_full_size_sampled():
     _score_sampled(ONETRANS_L, np.array([0, 1, 100, 201, 255]))
 
 
+def test_onetrans_l_block_forward_full_size():
+    # the bench's step (block_forward at the OneTrans-L shape, C = 256; S side on the caller's
+    # stream, NS side on the second stream gated by per-layer events) must reproduce scoring
+    # against a separately prefilled cache bit for bit for all 256 candidates, and the oracle
+    # on a sample
+    wl = ONETRANS_L
+    print(f"workload {wl.name}: block_forward C={wl.n_candidates}", flush=True)
+    mdl, lay = model(wl)
+    s, lens = make_s_tokens(wl)
+    ns = make_ns_tokens(wl)
+    sd, ld, nd = bf16_dev(s), torch.from_numpy(lens).cuda(), bf16_dev(ns)
+    for rep in range(3):  # repeated steps, as the bench runs them
+        t_bf, n_bf = mdl.block_forward(sd, ld, nd)
+    cache = mdl.new_cache(1)
+    tail = mdl.user_prefill(sd, ld, cache)
+    n_sc = mdl.score_candidates(cache, 0, nd[0])
+    torch.cuda.synchronize()
+    assert torch.equal(t_bf, tail)
+    assert torch.equal(n_bf[0], n_sc), "block_forward differs from scoring on a prefilled cache"
+    oc, ot = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[0], int(lens[0]))
+    assert_close(t_bf[0].cpu().numpy(), ot, "bf16", "S tail")
+    sample = np.array([0, 77, 128, 255])
+    assert_close(n_bf[0][sample].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, ns[0][sample]), "bf16",
+                 f"candidates {list(sample)}")
+
+
+@pytest.mark.parametrize("scale", [1e-4, 1e2])
+def test_scaled_inputs_match_oracle(scale):
+    # S and NS inputs scaled far from N(0, 1): the deferred RMSNorm keeps x * g in fp16, so
+    # small rows sit near the fp16 subnormal range and large rows near its top
+    wl, lens = SMALL["b_dh64_P32"]
+    print(f"case b_dh64_P32 scaled by {scale}", flush=True)
+    mdl, lay = model(wl)
+    s, lens, ns = _inputs(wl, lens)
+    s = bf16_round(s * scale)
+    ns = bf16_round(ns * scale)
+    s_out, ns_out = mdl.block_forward(*_dev(s, lens, ns))
+    torch.cuda.synchronize()
+    ref_t, ref_n = O.block_forward(lay, wl.q_sched, wl.n_heads, EPS, s, lens, ns)
+    assert_close(s_out.cpu().numpy(), ref_t, wl.ns_wdtype, "S tail")
+    assert_close(ns_out.cpu().numpy(), ref_n, wl.ns_wdtype, "NS out")
+
+
+@pytest.mark.timeout(600)
 def test_candidate_heavy_fp8_full_size_sampled():
-    _score_sampled(CANDIDATE_HEAVY_FP8, np.array([0, 511, 1024, 2047, 3000, 4095]))
+    # every 8th candidate (512 of 4096), each compared element by element with the oracle
+    _score_sampled(CANDIDATE_HEAVY_FP8, np.arange(0, CANDIDATE_HEAVY_FP8.n_candidates, 8))
 
 
 def test_onetrans_l_user_ns_full_size_sampled():

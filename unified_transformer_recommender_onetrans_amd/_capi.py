@@ -11,7 +11,9 @@ W_BF16, W_FP8_E4M3 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "buffer too small",
           4: "cache append capacity exceeded", 5: "HIP error"}
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libonetrans.so")
+# the in-tree build; ONETRANS_LIB names another build of the same sources (the host-sanitizer
+# build the ABI tests also run against)
+LIB_PATH = os.environ.get("ONETRANS_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libonetrans.so")
 
 
 class Config(ctypes.Structure):
@@ -64,6 +66,8 @@ EXPORTS = {
     "onetrans_kv_cache_read": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(KVCache), ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p]),
+    "onetrans_attention_route": (ctypes.c_char_p, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32]),
     "onetrans_kernel_timing_enable": (ctypes.c_int, [ctypes.c_uint32]),
     "onetrans_kernel_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                                    ctypes.POINTER(ctypes.c_int64)]),

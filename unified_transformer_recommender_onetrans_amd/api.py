@@ -77,6 +77,11 @@ class KVCache:
     def n_appended(self) -> int:
         return self.c.n_appended
 
+    @property
+    def prefilled(self) -> int:
+        """Users [0, prefilled) hold a prefill (0 before the first one)."""
+        return self.c.prefilled
+
     def read_layer(self, layer: int, user: int, rows: int):
         """K and V rows [0, rows) of one user and layer as bf16 [rows, d] tensors (heads concatenated)."""
         d = self.cfg.d_model
@@ -167,8 +172,9 @@ class OneTrans:
         return (out, un_out) if return_user_ns else out
 
     def kv_append(self, new_tokens: torch.Tensor, cache: KVCache) -> torch.Tensor:
+        """m new events for each prefilled user: new_tokens [cache.prefilled, m, d]."""
         cfg = self.cfg
-        B, m = cache.n_users, new_tokens.shape[1]
+        B, m = cache.prefilled, new_tokens.shape[1]
         _expect(new_tokens, "new_tokens", (B, m, cfg.d_model), torch.bfloat16, self.device)
         out = torch.empty(B, m, cfg.d_model, dtype=torch.float32, device=self.device)
         ws = self.workspace(lib().onetrans_workspace_bytes(ctypes.byref(cfg), B, 0, m))

@@ -920,51 +920,76 @@ void launch_attn_ns2(const AttnParams& p, int n_seg, hipStream_t s) {
   hipLaunchKernelGGL((attn_ns2_kernel<DH, NB>), grid, dim3(NB * 128), 0, s, p);
 }
 
-template <int NW>
-void launch_attn_nw(int dh, const AttnParams& p, int n_seg, hipStream_t s) {
+template <int DH, int NW>
+void launch_attn_nw(const AttnParams& p, int n_seg, hipStream_t s) {
   dim3 grid((p.nq + NW * 32 - 1) / (NW * 32), p.H, n_seg);
-  dim3 block(NW * 64);
-  if (dh == 64) hipLaunchKernelGGL((attn_kernel<64, NW>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_kernel<32, NW>), grid, block, 0, s, p);
+  hipLaunchKernelGGL((attn_kernel<DH, NW>), grid, dim3(NW * 64), 0, s, p);
+}
+
+// Which kernel instance runs a launch: 32 queries per wave, a workgroup's waves share the
+// K/V tiles. NS: each tile's keys split over two waves per query block, 2 query blocks (4
+// waves) per workgroup when there are blocks for 512 such workgroups, else 1. S: with few
+// query blocks (one user's prefill, appends) each block's keys are split over four waves,
+// the blocks of one (user, head) grouped on one XCD when there are several users; with many
+// (a batch of users' prefill) 4 or 2 query blocks share a workgroup's key stream. The K/V of
+// a layer is L2-resident, so streaming it to more workgroups is cheap.
+AttnRoute attention_route(bool ns, int dh, int nq, int H, int n_seg) {
+  const long blocks32 = (long)((nq + 31) / 32) * H * n_seg;
+  const bool d64 = dh == 64;
+  if (ns) {
+    if (blocks32 >= 2L * 512) return d64 ? ATTN_NS2_64_2 : ATTN_NS2_32_2;
+    return d64 ? ATTN_NS2_64_1 : ATTN_NS2_32_1;
+  }
+  if (blocks32 < 2L * 512) {
+    if (n_seg > 1) return d64 ? ATTN_SPLIT_64_GROUPED : ATTN_SPLIT_32_GROUPED;
+    return d64 ? ATTN_SPLIT_64 : ATTN_SPLIT_32;
+  }
+  if (blocks32 >= 4L * 512) return d64 ? ATTN_TILE_64_4 : ATTN_TILE_32_4;
+  return d64 ? ATTN_TILE_64_2 : ATTN_TILE_32_2;  // 1024 <= blocks32 < 2048
+}
+
+const char* attention_route_name(AttnRoute r) {
+  switch (r) {
+    case ATTN_NS2_64_2: return "attn_ns2_kernel<64,2>";
+    case ATTN_NS2_64_1: return "attn_ns2_kernel<64,1>";
+    case ATTN_NS2_32_2: return "attn_ns2_kernel<32,2>";
+    case ATTN_NS2_32_1: return "attn_ns2_kernel<32,1>";
+    case ATTN_SPLIT_64_GROUPED: return "attn_split_kernel<64,4,true>";
+    case ATTN_SPLIT_32_GROUPED: return "attn_split_kernel<32,4,true>";
+    case ATTN_SPLIT_64: return "attn_split_kernel<64,4,false>";
+    case ATTN_SPLIT_32: return "attn_split_kernel<32,4,false>";
+    case ATTN_TILE_64_4: return "attn_kernel<64,4>";
+    case ATTN_TILE_32_4: return "attn_kernel<32,4>";
+    case ATTN_TILE_64_2: return "attn_kernel<64,2>";
+    case ATTN_TILE_32_2: return "attn_kernel<32,2>";
+    default: return "none";
+  }
 }
 
 hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s) {
   if (p.nq <= 0 || n_seg <= 0) return hipSuccess;
   if (p.kv_cap % KT != 0 || (dh != 32 && dh != 64)) return hipErrorInvalidValue;
-  // 32 queries per wave; a workgroup's waves share the K/V tiles. Fewer waves per workgroup
-  // when the grid would leave CUs idle (one user's prefill has few query blocks per head);
-  // the K/V of a layer is L2-resident, so streaming it to more workgroups is cheap.
-  const long blocks32 = (long)((p.nq + 31) / 32) * p.H * n_seg;
-  if (ns) {
-    // NS: each tile's keys split over two waves per query block; 2 query blocks (4 waves)
-    // per workgroup when there are blocks for 512 such workgroups, else 1. Segments (their
-    // own cached keys each) come with no shared extra keys.
-    if (n_seg != 1 && p.n_x > 0) return hipErrorInvalidValue;
-    if (dh == 64) {
-      if (blocks32 >= 2L * 512) launch_attn_ns2<64, 2>(p, n_seg, s);
-      else launch_attn_ns2<64, 1>(p, n_seg, s);
-    } else {
-      if (blocks32 >= 2L * 512) launch_attn_ns2<32, 2>(p, n_seg, s);
-      else launch_attn_ns2<32, 1>(p, n_seg, s);
-    }
-  } else if (blocks32 < 2L * 512) {
-    // few S query blocks: split each block's keys over four waves; with several segments
-    // (users), the query blocks of one (user, head) grouped on one XCD
-    if (n_seg > 1) {
-      dim3 grid((p.nq + 31) / 32 * p.H * n_seg);
-      if (dh == 64) hipLaunchKernelGGL((attn_split_kernel<64, 4, true>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((attn_split_kernel<32, 4, true>), grid, dim3(256), 0, s, p);
-    } else {
-      dim3 grid((p.nq + 31) / 32, p.H, n_seg);
-      if (dh == 64) hipLaunchKernelGGL((attn_split_kernel<64, 4, false>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((attn_split_kernel<32, 4, false>), grid, dim3(256), 0, s, p);
-    }
-  } else if (blocks32 >= 4L * 512) {
-    launch_attn_nw<4>(dh, p, n_seg, s);
-  } else if (blocks32 >= 2L * 512) {
-    launch_attn_nw<2>(dh, p, n_seg, s);
-  } else {
-    launch_attn_nw<1>(dh, p, n_seg, s);
+  // NS segments (their own cached keys each) come with no shared extra keys
+  if (ns && n_seg != 1 && p.n_x > 0) return hipErrorInvalidValue;
+  const dim3 grouped_grid((p.nq + 31) / 32 * p.H * n_seg), split_grid((p.nq + 31) / 32, p.H, n_seg);
+  switch (attention_route(ns, dh, p.nq, p.H, n_seg)) {
+    case ATTN_NS2_64_2: launch_attn_ns2<64, 2>(p, n_seg, s); break;
+    case ATTN_NS2_64_1: launch_attn_ns2<64, 1>(p, n_seg, s); break;
+    case ATTN_NS2_32_2: launch_attn_ns2<32, 2>(p, n_seg, s); break;
+    case ATTN_NS2_32_1: launch_attn_ns2<32, 1>(p, n_seg, s); break;
+    case ATTN_SPLIT_64_GROUPED:
+      hipLaunchKernelGGL((attn_split_kernel<64, 4, true>), grouped_grid, dim3(256), 0, s, p);
+      break;
+    case ATTN_SPLIT_32_GROUPED:
+      hipLaunchKernelGGL((attn_split_kernel<32, 4, true>), grouped_grid, dim3(256), 0, s, p);
+      break;
+    case ATTN_SPLIT_64: hipLaunchKernelGGL((attn_split_kernel<64, 4, false>), split_grid, dim3(256), 0, s, p); break;
+    case ATTN_SPLIT_32: hipLaunchKernelGGL((attn_split_kernel<32, 4, false>), split_grid, dim3(256), 0, s, p); break;
+    case ATTN_TILE_64_4: launch_attn_nw<64, 4>(p, n_seg, s); break;
+    case ATTN_TILE_32_4: launch_attn_nw<32, 4>(p, n_seg, s); break;
+    case ATTN_TILE_64_2: launch_attn_nw<64, 2>(p, n_seg, s); break;
+    case ATTN_TILE_32_2: launch_attn_nw<32, 2>(p, n_seg, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -136,6 +136,16 @@ struct AttnParams {
 
 hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hipStream_t s);
 
+// The kernel instance launch_attention picks for nq queries per (segment, head).
+enum AttnRoute {
+  ATTN_NS2_64_2, ATTN_NS2_64_1, ATTN_NS2_32_2, ATTN_NS2_32_1,
+  ATTN_SPLIT_64_GROUPED, ATTN_SPLIT_32_GROUPED, ATTN_SPLIT_64, ATTN_SPLIT_32,
+  ATTN_TILE_64_4, ATTN_TILE_32_4, ATTN_TILE_64_2, ATTN_TILE_32_2,
+  ATTN_ROUTE_COUNT
+};
+AttnRoute attention_route(bool ns, int dh, int nq, int H, int n_seg);
+const char* attention_route_name(AttnRoute r);
+
 // Zeroes cache slots [from[l], cap[l]) of `blocks` (user, head) blocks of every layer l in
 // one launch: K [blocks][cap][dh] and V^T [blocks][dh][cap]. Key tiles that reach past
 // the filled length then read zeros.

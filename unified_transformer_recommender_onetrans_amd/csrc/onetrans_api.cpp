@@ -741,7 +741,7 @@ int onetrans_user_prefill(const onetrans_config* cfg, const void* packed, const 
                     ns_user_tokens, s_out, ns_user_out, (char*)workspace, stream);
   if (rc) return rc;
   cache->n_appended = 0;
-  cache->prefilled = 1;
+  cache->prefilled = B;
   return ONETRANS_OK;
 }
 
@@ -753,15 +753,16 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
   if (rc) return rc;
   if (!packed || !cache || !cache->buf) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
   if ((rc = check_cache_key(cfg, cache))) return rc;
-  if (!cache->prefilled) return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
+  if (cache->prefilled < 1 || cache->prefilled > cache->n_users)
+    return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
   if (m < 0) return fail(ONETRANS_ERR_INVALID_ARG, "m must be >= 0");
   if (cache->n_appended + (long)m > s.append_cap) return fail(ONETRANS_ERR_CAPACITY, "append exceeds append_cap");
   if (m == 0) return ONETRANS_OK;
   if (!new_tokens || !new_out || !workspace) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
   if (!aligned16(packed) || !aligned16(new_tokens) || !aligned16(new_out) || !aligned16(workspace))
     return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
-  const int B = cache->n_users;
-  if (cache->bytes < cache_layout(s, B, nullptr, nullptr))
+  const int B = cache->prefilled;  // users [0, B) hold a prefill; the layout is that of n_users
+  if (cache->bytes < cache_layout(s, cache->n_users, nullptr, nullptr))
     return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
   const AppendWs w = append_ws(s, B, m);
   if (workspace_bytes < append_need(s, B, m)) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for append");
@@ -769,7 +770,7 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
   packed_layout(s, lo);
   size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
   UserNsOff un;
-  cache_layout(s, B, k_off, v_off, &un);
+  cache_layout(s, cache->n_users, k_off, v_off, &un);
   char* cb = (char*)cache->buf;
   char* ws = (char*)workspace;
   _Float16* xn = (_Float16*)(ws + w.xn);
@@ -811,8 +812,9 @@ int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, co
   if (rc) return rc;
   if (!packed || !cache || !cache->buf) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
   if ((rc = check_cache_key(cfg, cache))) return rc;
-  if (!cache->prefilled) return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
-  if (user < 0 || user >= cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "user out of range");
+  if (cache->prefilled < 1 || cache->prefilled > cache->n_users)
+    return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
+  if (user < 0 || user >= cache->prefilled) return fail(ONETRANS_ERR_INVALID_ARG, "user out of range (not prefilled)");
   if (C < 0) return fail(ONETRANS_ERR_INVALID_ARG, "C must be >= 0");
   if (C == 0) return ONETRANS_OK;
   if (!ns_tokens || !ns_out || !workspace) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
@@ -902,7 +904,8 @@ int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* 
   if (!cache || !cache->buf || !k_out || !v_out) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
   if ((rc = check_cache_key(cfg, cache))) return rc;
   if (layer < 0 || layer >= s.L) return fail(ONETRANS_ERR_INVALID_ARG, "layer out of range");
-  if (user < 0 || user >= cache->n_users) return fail(ONETRANS_ERR_INVALID_ARG, "user out of range");
+  if (user < 0 || user >= cache->prefilled || cache->prefilled > cache->n_users)
+    return fail(ONETRANS_ERR_INVALID_ARG, "user out of range (not prefilled)");
   if (rows < 0 || rows > s.n[layer] + cache->n_appended) return fail(ONETRANS_ERR_INVALID_ARG, "rows beyond the filled length");
   size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
   cache_layout(s, cache->n_users, k_off, v_off);
@@ -912,6 +915,12 @@ int onetrans_kv_cache_read(const onetrans_config* cfg, const onetrans_kv_cache* 
                            s.cap[layer], rows, (__bf16*)k_out, (__bf16*)v_out, stream),
          "cache read launch");
   return ONETRANS_OK;
+}
+
+const char* onetrans_attention_route(int32_t ns, int32_t head_dim, int32_t n_queries, int32_t n_heads,
+                                     int32_t n_seg) {
+  if ((head_dim != 32 && head_dim != 64) || n_queries < 1 || n_heads < 1 || n_seg < 1) return "none";
+  return attention_route_name(attention_route(ns != 0, head_dim, n_queries, n_heads, n_seg));
 }
 
 int onetrans_kernel_timing_enable(uint32_t mask) {
