@@ -222,6 +222,23 @@ int onetrans_score_candidates(const onetrans_config* cfg, const void* packed,
                               const uint16_t* ns_tokens, int32_t C, float* ns_out,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Allocation-free scoring, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same computation and arguments as onetrans_score_candidates without the
+ * workspace: its scratch is one static device array of ONETRANS_NOALLOC_SCRATCH_BYTES per
+ * GPU, which the library holds from the first call on that GPU until the process ends.
+ * The call allocates nothing (no hipMalloc, no library allocation). Returns
+ * ONETRANS_ERR_WORKSPACE with no launch when the call needs more scratch than that
+ * (the need is onetrans_workspace_bytes(cfg, 0, C, 0); at the OneTrans-L shape, 256
+ * candidates of 32 NS rows need about 51 MB). Calls that overlap on one GPU (concurrent
+ * streams, threads) share the array and race; serialise them. Nothing in the array
+ * needs to start at zero, so its contents from an earlier call are harmless. */
+#define ONETRANS_NOALLOC_SCRATCH_BYTES (64u << 20)
+int onetrans_score_candidates_noalloc(const onetrans_config* cfg, const void* packed,
+                                      const onetrans_kv_cache* cache, int32_t user,
+                                      const uint16_t* ns_tokens, int32_t C, float* ns_out,
+                                      hipStream_t stream);
+
 /* Block forward (agihunt.info OneTrans summary, block and pyramid / KV paragraphs).
  * Full pass without a persistent cache: prefill of B users into a cache held
  * in the workspace, then scoring of each user's C candidates.

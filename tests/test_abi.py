@@ -229,3 +229,22 @@ def test_status_strings(lib):
     for code in range(6):
         assert lib.onetrans_status_str(code).decode()
     assert lib.onetrans_status_str(99).decode() == "unknown status"
+
+
+def test_noalloc_scoring_rejects_before_any_device_work(lib):
+    # the allocation-free scoring call: the same checks as scoring, and a clear error when
+    # the call needs more than the static scratch holds (no launch, no device query)
+    cfg = l_cfg()
+    F = 1 << 41
+    c = _cache(lib, cfg)
+    f = lib.onetrans_score_candidates_noalloc
+    assert f(ctypes.byref(cfg), F, ctypes.byref(c), 0, F, 0, F, None) == OK          # nothing to do
+    assert f(ctypes.byref(cfg), F, ctypes.byref(c), 1, F, 8, F, None) == INVALID     # user not prefilled
+    assert f(ctypes.byref(cfg), F, ctypes.byref(c), 0, F + 2, 8, F, None) == INVALID
+    assert f(ctypes.byref(cfg), None, ctypes.byref(c), 0, F, 8, F, None) == INVALID
+    need = lib.onetrans_workspace_bytes(ctypes.byref(cfg), 0, 4096, 0)
+    assert need > 64 << 20
+    assert f(ctypes.byref(cfg), F, ctypes.byref(c), 0, F, 4096, F, None) == WORKSPACE
+    msg = lib.onetrans_last_error().decode()
+    assert "scratch" in msg and str(64 << 20) in msg
+    assert lib.onetrans_workspace_bytes(ctypes.byref(cfg), 0, 256, 0) <= 64 << 20  # the L shape's C = 256 fits

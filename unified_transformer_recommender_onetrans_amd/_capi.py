@@ -57,6 +57,9 @@ EXPORTS = {
     "onetrans_score_candidates": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_void_p, ctypes.POINTER(KVCache),
                                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "onetrans_score_candidates_noalloc": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_void_p,
+                                                         ctypes.POINTER(KVCache), ctypes.c_int32, ctypes.c_void_p,
+                                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "onetrans_block_forward": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

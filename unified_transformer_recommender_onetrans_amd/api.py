@@ -197,6 +197,21 @@ class OneTrans:
                                               _stream(self.device)), "score_candidates")
         return out
 
+    def score_candidates_noalloc(self, cache: KVCache, user: int, ns_tokens: torch.Tensor,
+                                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """score_candidates through the allocation-free entry point (the library's static
+        per-GPU scratch instead of a workspace; no device allocation when `out` is given)."""
+        cfg = self.cfg
+        Cn, Pc = ns_tokens.shape[0], self.n_cand_ns
+        _expect(ns_tokens, "ns_tokens", (Cn, Pc, cfg.d_model), torch.bfloat16, self.device)
+        if out is None:
+            out = torch.empty(Cn, Pc, cfg.d_model, dtype=torch.float32, device=self.device)
+        _expect(out, "ns_out", (Cn, Pc, cfg.d_model), torch.float32, self.device)
+        check(lib().onetrans_score_candidates_noalloc(ctypes.byref(cfg), self.packed.data_ptr(), ctypes.byref(cache.c),
+                                                      user, ns_tokens.data_ptr(), Cn, out.data_ptr(),
+                                                      _stream(self.device)), "score_candidates_noalloc")
+        return out
+
     def block_forward(self, s_tokens: torch.Tensor, s_lens: torch.Tensor, ns_tokens: torch.Tensor,
                       ns_user_tokens: Optional[torch.Tensor] = None):
         cfg = self.cfg

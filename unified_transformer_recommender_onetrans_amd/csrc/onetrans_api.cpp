@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -804,10 +805,15 @@ int onetrans_kv_append(const onetrans_config* cfg, const void* packed, const uin
   return user_ns_impl(s, (const char*)packed, lo, cb, k_off, v_off, un, B, cache->n_appended, nullptr, ws, stream);
 }
 
-int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, const onetrans_kv_cache* cache,
-                              int32_t user, const uint16_t* ns_tokens, int32_t C, float* ns_out, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream) {
-  Shape s;
+}  // extern "C"
+
+namespace {
+
+// Host checks of a scoring call (no device work). *done is set when there is nothing to
+// launch (C == 0).
+int score_check(const onetrans_config* cfg, Shape& s, const void* packed, const onetrans_kv_cache* cache, int32_t user,
+                const uint16_t* ns_tokens, int32_t C, float* ns_out, bool* done) {
+  *done = false;
   int rc = make_shape(cfg, s);
   if (rc) return rc;
   if (!packed || !cache || !cache->buf) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
@@ -816,14 +822,21 @@ int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, co
     return fail(ONETRANS_ERR_INVALID_ARG, "cache has not been prefilled");
   if (user < 0 || user >= cache->prefilled) return fail(ONETRANS_ERR_INVALID_ARG, "user out of range (not prefilled)");
   if (C < 0) return fail(ONETRANS_ERR_INVALID_ARG, "C must be >= 0");
-  if (C == 0) return ONETRANS_OK;
-  if (!ns_tokens || !ns_out || !workspace) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
-  if (!aligned16(packed) || !aligned16(ns_tokens) || !aligned16(ns_out) || !aligned16(workspace))
+  if (C == 0) {
+    *done = true;
+    return ONETRANS_OK;
+  }
+  if (!ns_tokens || !ns_out) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(packed) || !aligned16(ns_tokens) || !aligned16(ns_out))
     return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
   if ((long)C * s.Pc > (1L << 26)) return fail(ONETRANS_ERR_UNSUPPORTED, "C * (n_ns - n_ns_user) must be <= 2^26");
   if (cache->bytes < cache_layout(s, cache->n_users, nullptr, nullptr))
     return fail(ONETRANS_ERR_WORKSPACE, "cache buffer smaller than its n_users needs");
-  if (workspace_bytes < score_ws(s, C, s.Pc).total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for scoring");
+  return ONETRANS_OK;
+}
+
+int score_run(const Shape& s, const void* packed, const onetrans_kv_cache* cache, int32_t user,
+              const uint16_t* ns_tokens, int32_t C, float* ns_out, char* ws, hipStream_t stream) {
   LayerOffsets lo[ONETRANS_MAX_LAYERS];
   packed_layout(s, lo);
   size_t k_off[ONETRANS_MAX_LAYERS], v_off[ONETRANS_MAX_LAYERS];
@@ -831,7 +844,65 @@ int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, co
   cache_layout(s, cache->n_users, k_off, v_off, &un);
   char* cb = (char*)cache->buf;
   return score_impl(s, (const char*)packed, lo, cb, k_off, v_off, cache->n_appended, user,
-                    candidate_pass(s, cb, un, user), ns_tokens, C, ns_out, (char*)workspace, stream);
+                    candidate_pass(s, cb, un, user), ns_tokens, C, ns_out, ws, stream);
+}
+
+// ---- scratch of the allocation-free scoring call ----
+// One array per GPU the library runs on, held until the process ends. Host code never uses
+// the name `scratch` as an address (on the host it only stands in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) char scratch[ONETRANS_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(char** out) {
+  int dev = 0;
+  OT_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ONETRANS_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    OT_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch symbol address");
+    if (!p) return fail(ONETRANS_ERR_HIP, "scratch symbol address is NULL");
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ONETRANS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int onetrans_score_candidates(const onetrans_config* cfg, const void* packed, const onetrans_kv_cache* cache,
+                              int32_t user, const uint16_t* ns_tokens, int32_t C, float* ns_out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  bool done = false;
+  int rc = score_check(cfg, s, packed, cache, user, ns_tokens, C, ns_out, &done);
+  if (rc || done) return rc;
+  if (!workspace) return fail(ONETRANS_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(workspace)) return fail(ONETRANS_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if (workspace_bytes < score_ws(s, C, s.Pc).total) return fail(ONETRANS_ERR_WORKSPACE, "workspace too small for scoring");
+  return score_run(s, packed, cache, user, ns_tokens, C, ns_out, (char*)workspace, stream);
+}
+
+int onetrans_score_candidates_noalloc(const onetrans_config* cfg, const void* packed, const onetrans_kv_cache* cache,
+                                      int32_t user, const uint16_t* ns_tokens, int32_t C, float* ns_out,
+                                      hipStream_t stream) {
+  Shape s;
+  bool done = false;
+  int rc = score_check(cfg, s, packed, cache, user, ns_tokens, C, ns_out, &done);
+  if (rc || done) return rc;
+  const size_t need = score_ws(s, C, s.Pc).total;
+  if (need > (size_t)ONETRANS_NOALLOC_SCRATCH_BYTES)
+    return fail(ONETRANS_ERR_WORKSPACE, "scoring " + std::to_string(C) + " candidates needs " + std::to_string(need) +
+                                            " bytes of scratch; the allocation-free call holds " +
+                                            std::to_string((size_t)ONETRANS_NOALLOC_SCRATCH_BYTES) +
+                                            " (score fewer candidates per call, or use onetrans_score_candidates)");
+  char* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  return score_run(s, packed, cache, user, ns_tokens, C, ns_out, ws, stream);
 }
 
 int onetrans_block_forward(const onetrans_config* cfg, const void* packed, const uint16_t* s_tokens,
