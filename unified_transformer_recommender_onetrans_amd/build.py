@@ -18,14 +18,16 @@ ARCH = "gfx950"
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
          # no packed-fp32 instructions: plain scalar fp32 code only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         # MFMA accumulators in ordinary VGPRs: no copies between AGPRs and VGPRs
-         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", INCLUDE, "-Wno-unused-result"]
+# MFMA accumulators in ordinary VGPRs: no copies between AGPRs and VGPRs (a source may
+# opt out through SOURCE_FLAGS)
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCE_FLAGS = {}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, VGPR_FORM) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

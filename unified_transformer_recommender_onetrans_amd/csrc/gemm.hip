@@ -36,84 +36,10 @@
 // lane ends up holding one output row and groups of four consecutive columns, so the
 // epilogue writes 16 contiguous bytes per lane and instruction. E4M3 weights are
 // decoded to fp16 exactly in registers after the LDS read.
-#include "internal.h"
+#include "gemm_common.h"
 
 namespace onetrans {
 namespace {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int N_XCD = 8;
-
-__device__ __forceinline__ long res_row_off(const RowMap& rm, int seg, int t, int g) {
-  return (long)seg * rm.res_seg_stride + (rm.res_row_base + t) * rm.res_row_stride + (long)g * rm.res_group_stride;
-}
-__device__ __forceinline__ long hid_row(const RowMap& rm, int seg, int t, int g) {
-  return ((long)seg * rm.rows_per_seg + t) * rm.row_mult + g;
-}
-// row -> (seg, t) without an integer division: float estimate, then one correction
-__device__ __forceinline__ void split_row(int row, int rps, float inv_rps, int& seg, int& t) {
-  seg = (int)((float)row * inv_rps);
-  t = row - seg * rps;
-  if (t < 0) { --seg; t += rps; }
-  else if (t >= rps) { ++seg; t -= rps; }
-}
-
-// 8 OCP E4M3FN codes (two dwords, code i in byte i) -> 8 halfs in order, with the gfx950
-// conversion instruction at scale 1, which is exact: every E4M3FN value, subnormals
-// included, is an fp16 value.
-__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint2 c) {
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.0f, false);
-  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.0f, true);
-  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.0f, false);
-  const f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.0f, true);
-  const f16x8 r = {a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
-  return r;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-// Wait until at most `later` k-tiles of PT loads each are still in flight. Only loads
-// are counted: loads retire in order, so a pending store can delay this wait but never
-// satisfy it early.
-template <int PT, int MAXL>
-__device__ __forceinline__ void wait_tiles(int later) {
-  if constexpr (MAXL == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (later >= MAXL) wait_vmcnt<PT * MAXL>();
-    else wait_tiles<PT, MAXL - 1>(later);
-  }
-}
-
-// Workgroup barrier without the release fence __syncthreads() carries (which
-// would wait for every load in flight, draining the pipeline). The explicit
-// vmcnt waits before it make the DMA'd tile visible; the empty asm statements
-// keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  // this wave's LDS reads have returned (lgkmcnt 0; vmcnt and expcnt unconstrained): the
-  // loaders refill the stage read last right after the barrier, and the compiler may defer
-  // a fragment read's wait to its MFMA, past the barrier
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// physical 16-byte chunk of logical chunk c in LDS row r (rows of ROWB bytes)
-template <int ROWB>
-__device__ __forceinline__ int swz(int c, int r) {
-  static_assert(ROWB == 64 || ROWB == 128, "row size");
-  return ROWB == 128 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
-}
 
 // SIDE (0 = shared S weights, 1 = private NS weights) only names the instance.
 // Waves 0-3 compute (a WM x (4/WM) grid over the tile), waves 4-7 load.
@@ -212,6 +138,36 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
 
   // ================= compute waves: MFMA and epilogue stores, never wait for operand loads =================
   const int wm = wave / WN, wn = wave % WN;
+  constexpr int KS = BK / 16;  // 16-wide k-steps per k-tile (even: the fragment buffers alternate)
+  static_assert(KS % 2 == 0, "k-steps per tile");
+  // Fragments of one k-step, double-buffered: the reads of step ks + 1 are issued before the
+  // MFMAs of step ks, so LDS latency hides under them. E4M3 weights stay as codes until the
+  // MFMA that takes them.
+  f16x8 af[2][MI];
+  f16x8 bf[2][FP8 ? 1 : NI];
+  uint2 b8[2][FP8 ? NI : 1];
+  auto read_frags = [&](int s, int ks, int b) {
+    const char* st = smem + (s % STAGES) * STAGE;
+    const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = wm * TM + mi * 32 + (lane & 31);
+      af[b][mi] = *(const f16x8*)(st + r * AROW + (swz<AROW>(c, r) << 4));
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int r = wn * TN + ni * 32 + (lane & 31);
+      if constexpr (FP8)
+        b8[b][ni] = *(const uint2*)(st + A_BYTES + r * 64 + (swz<64>(ks, r) << 4) + (lane >> 5) * 8);
+      else
+        bf[b][ni] = *(const f16x8*)(st + A_BYTES + r * BROW + (swz<BROW>(c, r) << 4));
+    }
+  };
+  // the first step's tile is in LDS (one barrier per step, as the loaders)
+  if (my_items > 0) {
+    lds_barrier();
+    read_frags(0, 0, 0);
+  }
 #pragma unroll 1
   for (int t = 0; t < my_items; ++t) {
     f32x16 acc[MI][NI];
@@ -222,265 +178,43 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
-    // deferred RMSNorm (QKV, FFN up): load this item's row partials now, so that they have
-    // arrived by the epilogue. Chunks of four partials alternate between the half-waves;
-    // chunks 0-3 (16 partials) are held through the k-loop, any beyond load in the epilogue.
-    const float* ss_rows[MI];
-    float4 ss_raw[MI][2];
-    if (KIND != GEMM_FFN_DOWN && p.ss_in) {
-      const int w = ib + t * nx;
-      int mt, nt, g;
-      tile_of(w, mt, nt, g);
-      const int last_chunk = p.ss_stride / 4 - 1;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = min(mt * BM + wm * TM + mi * 32 + (lane & 31), M - 1);
-        int seg, tt;
-        split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
-        ss_rows[mi] = p.ss_in + hid_row(rm, seg, tt, g) * p.ss_stride;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) ss_raw[mi][j] = *(const float4*)(ss_rows[mi] + 4 * min(2 * j + (lane >> 5), last_chunk));
-      }
-    }
-    // FFN down with few accumulator blocks per wave: load the residual rows of this item now
-    // as well (each element belongs to one item, so nothing writes them in between)
-    constexpr bool X_EARLY = KIND == GEMM_FFN_DOWN && MI * NI <= 3;
-    float4 x_pre[X_EARLY ? MI : 1][X_EARLY ? NI : 1][4];
-    if constexpr (X_EARLY) {
-      const int w = ib + t * nx;
-      int mt, nt, g;
-      tile_of(w, mt, nt, g);
-      const int col = nt * BN + wn * TN + 4 * (lane >> 5);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = min(mt * BM + wm * TM + mi * 32 + (lane & 31), M - 1);
-        int seg, tt;
-        split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
-        const float* rrow = p.res_out + res_row_off(rm, seg, tt, g) + col;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) x_pre[mi][ni][q] = *(const float4*)(rrow + ni * 32 + 8 * q);
-      }
-    }
-    // the partials of chunk c4 that exist (the rest of a row's slots may hold stale data)
-    auto chunk_sum = [&](float4 v, int c4) {
-      const int b = 4 * c4, n = p.ss_parts;
-      return (b < n ? v.x : 0.f) + (b + 1 < n ? v.y : 0.f) + (b + 2 < n ? v.z : 0.f) + (b + 3 < n ? v.w : 0.f);
-    };
+    int mt_, nt_, g_;
+    tile_of(ib + t * nx, mt_, nt_, g_);
+    TilePre<KIND, MI, NI> pre;
+    tile_prefetch<KIND, MI, NI, TM, TN>(p, mt_ * BM, nt_ * BN, g_, wm, wn, pre);
 
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
       const int s = t * nk + kt;
-      lds_barrier();  // step s is in LDS
-      const char* st = smem + (s % STAGES) * STAGE;
-      // Fragments of a group of 16-wide k-steps are all read before its MFMAs: with one
-      // register set per k-step the reads of step ks + 1 could only start after step ks's
-      // MFMAs had consumed the registers, exposing the LDS latency at every k-step.
-      constexpr int KS = BK / 16;
-      constexpr int FG = MI + NI <= 4 ? KS : KS / 2;  // k-steps per group (register budget)
 #pragma unroll
-      for (int g0 = 0; g0 < KS; g0 += FG) {
-        f16x8 a[FG][MI];
-        f16x8 b[FG][NI];
-        uint2 b8[FG][NI];
-#pragma unroll
-        for (int kk = 0; kk < FG; ++kk) {
-          const int ks = g0 + kk;
-          const int c = 2 * ks + (lane >> 5);
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi) {
-            const int r = wm * TM + mi * 32 + (lane & 31);
-            a[kk][mi] = *(const f16x8*)(st + r * AROW + (swz<AROW>(c, r) << 4));
-          }
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            const int r = wn * TN + ni * 32 + (lane & 31);
-            if (FP8)
-              b8[kk][ni] = *(const uint2*)(st + A_BYTES + r * 64 + (swz<64>(ks, r) << 4) + (lane >> 5) * 8);
-            else
-              b[kk][ni] = *(const f16x8*)(st + A_BYTES + r * BROW + (swz<BROW>(c, r) << 4));
-          }
+      for (int ks = 0; ks < KS; ++ks) {
+        const int b = ks & 1;
+        // this step's fragments, read one step ago, have arrived; waiting before the next
+        // reads are issued keeps the compiler from waiting for those as well
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        if (ks + 1 < KS) {
+          read_frags(s, ks + 1, b ^ 1);
+        } else if (s + 1 < total_steps) {
+          // every wave has read its last fragments of step s: the barrier hands that stage
+          // back to the loaders and certifies step s + 1, whose first fragments are read now
+          lds_barrier();
+          read_frags(s + 1, 0, b ^ 1);
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep every read of the group ahead of its MFMAs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < FG; ++kk) {
-          if (FP8) {
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) b[kk][ni] = e4m3x8_to_f16(b8[kk][ni]);
-          }
+        for (int ni = 0; ni < NI; ++ni) {
+          f16x8 wf;
+          if constexpr (FP8) wf = e4m3x8_to_f16(b8[b][ni]);
+          else wf = bf[b][ni];
 #pragma unroll
           for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[kk][ni], a[kk][mi], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, af[b][mi], acc[mi][ni], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // ---- epilogue. With the weight fragment first in the MFMA, lane holds output row
-    // (lane % 32) of each 32x32 block and, in registers 4q..4q+3, columns
-    // 8q + 4*(lane/32) + 0..3. ----
-    const int w = ib + t * nx;
-    int mt, nt, g;
-    tile_of(w, mt, nt, g);
-    const int m0 = mt * BM, n0 = nt * BN;
-    const float scale = FP8 ? p.wscale[g * 5 + p.scale_idx0 + n0 / p.scale_col_div] : 1.f;
-    const int half = lane >> 5;
-    const int col_l = n0 + wn * TN;                // + ni*32 + 8q + 4*half
-    const int row_l = m0 + wm * TM + (lane & 31);  // + mi*32
-    if (KIND == GEMM_FFN_DOWN) {
-      // fp32 residual rows: read-modify-write 16 bytes per (block, register group); then
-      // the next norm's operand x * g and one partial sum of squares per 32 columns
-      const NormOut& no = p.nout;
-      // the gains (the same columns for every row) before any store: a wait for a load
-      // issued after a store also waits for that store
-      float4 gv[NI][4];
-      if (no.xg) {
-        const float* grow = no.gain + (long)g * no.gain_group_stride + col_l + 4 * half;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) gv[ni][q] = *(const float4*)(grow + ni * 32 + 8 * q);
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = row_l + mi * 32;
-        if (row >= M) continue;  // both half-waves hold the same row
-        int seg, tt;
-        split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
-        float* rrow = p.res_out + res_row_off(rm, seg, tt, g) + col_l + 4 * half;
-        float4 x[NI][4];
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if constexpr (X_EARLY) x[ni][q] = x_pre[mi][ni][q];
-            else x[ni][q] = *(const float4*)(rrow + ni * 32 + 8 * q);
-          }
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x16& a = acc[mi][ni];
-            float4& v = x[ni][q];
-            v.x += a[4 * q + 0] * scale;
-            v.y += a[4 * q + 1] * scale;
-            v.z += a[4 * q + 2] * scale;
-            v.w += a[4 * q + 3] * scale;
-            *(float4*)(rrow + ni * 32 + 8 * q) = v;
-          }
-        if (no.xg) {
-          const long hr = hid_row(rm, seg, tt, g);
-          _Float16* xrow = no.xg + hr * N + col_l + 4 * half;
-          float* srow = no.ss + hr * no.ss_stride + (col_l >> 5);
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            float part = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 v = x[ni][q], gg = gv[ni][q];
-              part += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-              const f16x4 o = {(_Float16)(v.x * gg.x), (_Float16)(v.y * gg.y), (_Float16)(v.z * gg.z),
-                               (_Float16)(v.w * gg.w)};
-              *(f16x4*)(xrow + ni * 32 + 8 * q) = o;
-            }
-            part += other_half(part);
-            if (half == 0) srow[ni] = part;
-          }
-        }
-      }
-    } else {
-      // ---- 16-bit outputs (Q / K / V, GELU hidden rows), straight from registers. Packed
-      // to 16-bit pairs, groups q and q+1 trade halves across the two half-waves
-      // (v_permlane32_swap), after which a lane holds 8 consecutive columns of one group:
-      // one 16-byte store each. Rows are scaled by the deferred RMSNorm factor. ----
-      auto pack2 = [&](float x, float y) -> uint32_t {
-        if (KIND == GEMM_FFN_UP) {
-          const _Float16 hx = (_Float16)x, hy = (_Float16)y;
-          return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
-        }
-        const __bf16 bx = (__bf16)x, by = (__bf16)y;
-        return (uint32_t)__builtin_bit_cast(uint16_t, bx) | ((uint32_t)__builtin_bit_cast(uint16_t, by) << 16);
-      };
-      const int typ = KIND == GEMM_QKV ? n0 / p.d : 0;
-      const bool vt_mode = KIND == GEMM_QKV && typ == 2 && p.vt != nullptr;
-      const int dsh = p.dh == 64 ? 6 : 5;
-      // every row factor before the first store: on gfx9 a wait for a load issued
-      // after a store also waits for that store
-      float srow[MI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        srow[mi] = scale;
-        if (p.ss_in) {
-          float sum = chunk_sum(ss_raw[mi][0], half) + chunk_sum(ss_raw[mi][1], 2 + half);
-          for (int c4 = 4 + half; 4 * c4 < p.ss_parts; c4 += 2) sum += chunk_sum(*(const float4*)(ss_rows[mi] + 4 * c4), c4);
-          sum += other_half(sum);
-          srow[mi] *= 1.0f / sqrtf(sum / (float)K + p.eps);
-        }
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = row_l + mi * 32;
-        if (row >= M) continue;
-        int seg, tt;
-        split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
-        const float sr = srow[mi];
-        auto val = [&](float x) { return KIND == GEMM_FFN_UP ? gelu_as(x * sr) : x * sr; };
-        if (vt_mode) {
-          // transposed V: lanes hold 32 consecutive key slots of each column
-          __bf16* base = p.vt + seg * p.kv_seg_stride + p.kv_slot_base + (long)tt * rm.row_mult + g;
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int cc = col_l - typ * p.d + ni * 32 + 8 * q + 4 * half + e;
-                base[(cc >> dsh) * p.kv_head_stride + (long)(cc & (p.dh - 1)) * p.kv_cap] =
-                    (__bf16)val(acc[mi][ni][4 * q + e]);
-              }
-          continue;
-        }
-        long rbase;  // element offset of this row's first column (16-bit outputs)
-        long head_stride = 0;
-        __bf16* out = nullptr;
-        if (KIND == GEMM_FFN_UP) {
-          rbase = hid_row(rm, seg, tt, g) * N;
-        } else {
-          const long ti = (long)tt * rm.row_mult + g;
-          if (typ == 0) {
-            if (ti < p.q_from) continue;
-            rbase = seg * p.q_seg_stride + (ti - p.q_from) * p.dh;
-            head_stride = p.q_head_stride;
-            out = p.q;
-          } else {
-            rbase = seg * p.kv_seg_stride + (p.kv_slot_base + ti) * p.dh;
-            head_stride = p.kv_head_stride;
-            out = typ == 1 ? p.k : p.v;
-          }
-        }
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int qq = 0; qq < 4; qq += 2) {
-            const f32x16& v = acc[mi][ni];
-            const int j0 = 4 * qq, j1 = 4 * qq + 4;
-            const auto lo = __builtin_amdgcn_permlane32_swap(pack2(val(v[j0]), val(v[j0 + 1])),
-                                                             pack2(val(v[j1]), val(v[j1 + 1])), false, false);
-            const auto hi = __builtin_amdgcn_permlane32_swap(pack2(val(v[j0 + 2]), val(v[j0 + 3])),
-                                                             pack2(val(v[j1 + 2]), val(v[j1 + 3])), false, false);
-            const uint4 chunk = make_uint4(lo[0], hi[0], lo[1], hi[1]);
-            const int c = col_l + ni * 32 + 8 * (qq + half);
-            if (KIND == GEMM_FFN_UP) {
-              *(uint4*)(p.hid_out + rbase + c) = chunk;
-            } else {
-              const int cc = c - typ * p.d;
-              *(uint4*)(out + rbase + (cc >> dsh) * head_stride + (cc & (p.dh - 1))) = chunk;
-            }
-          }
-      }
-    }
+    tile_epilogue<KIND, FP8, MI, NI, TM, TN>(p, acc, mt_ * BM, nt_ * BN, g_, wm, wn, pre);
   }
 }
 

@@ -9,7 +9,7 @@ from __future__ import annotations
 import os
 import subprocess
 
-from .build import ARCH, BUILD_DIR, CSRC, FLAGS, HIPCC, SOURCES, build
+from .build import ARCH, BUILD_DIR, CSRC, FLAGS, HIPCC, SOURCES, VGPR_FORM, build
 
 ASAN_RUNTIME = "/opt/rocm/lib/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so"
 SANITIZED_LIB = os.path.join(BUILD_DIR, "asan", "libonetrans_asan.so")
@@ -26,7 +26,7 @@ def build_sanitized(verbose: bool = False) -> str:
         build()
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
     api = os.path.join(os.path.dirname(SANITIZED_LIB), "onetrans_api.o")
-    cmd = ([HIPCC] + [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"] + san +
+    cmd = ([HIPCC] + [f for f in FLAGS if f != "-O3"] + VGPR_FORM + ["-O1", "-g"] + san +
            ["-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
             "-c", os.path.join(CSRC, "onetrans_api.cpp"), "-o", api])
     r = subprocess.run(cmd, capture_output=True, text=True)
