@@ -14,8 +14,9 @@
 // operand is a plain row read.
 //
 // Data movement: each wave owns 32 queries; a workgroup of 4 waves shares K and
-// V^T tiles of 64 keys that travel global -> LDS with global_load_lds_dwordx4,
-// three tiles in flight. Tile rows are XOR-swizzled in 16-byte chunks so the
+// V^T tiles of 64 keys that travel global -> LDS with buffer_load_dwordx4 ... lds
+// (base in a buffer resource, so no per-lane 64-bit address arithmetic), three tiles in
+// flight. Tile rows are XOR-swizzled in 16-byte chunks so the
 // fragment reads are bank-conflict free. The result is added to the fp32
 // residual rows (z = x + o) without rounding.
 #include <math.h>
@@ -60,19 +61,21 @@ struct Softmax {
 // SUM false the caller adds the probabilities' sum to l itself (attn_tile does it on the
 // matrix core).
 // The scale 1/sqrt(dh) * log2(e) is applied inside exp2 as one fma. The O
-// accumulators are rescaled only when some lane's running max grew: otherwise
-// the factor is exactly 1 and the multiply is skipped. Returns the bf16
-// probabilities packed as the B operands of the P.V product.
-template <int DH, int NB, bool SUM = true>
+// accumulators are rescaled only when some lane's reference max moved: otherwise
+// the factor is exactly 1 and the multiply is skipped. Without LAZY the reference is the
+// running max; with LAZY it moves only when a block's max exceeds it by more than 8 in
+// log2 units (probabilities then stay below 2^8; any reference gives the same normalised
+// result), so after the first keys of a query the rescale is almost never taken, where
+// the running max of some lane of a wave grows at nearly every tile of a long key range.
+// Returns the bf16 probabilities packed as the B operands of the P.V product.
+template <int DH, int NB, bool SUM = true, bool LAZY = false>
 __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&sc)[NB], bf16x8 (&pb)[NB][2],
                                                float scale) {
-  float mt = -INFINITY;
+  float mt = vmax16(sc[0]);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sc[b][j]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  const float m_new = fmaxf(st.m, mt);
+  for (int b = 1; b < NB; ++b) mt = vmax(mt, vmax16(sc[b]));
+  mt = max_halves(mt);
+  const float m_new = LAZY ? (mt > st.m + 8.f / scale ? mt : st.m) : fmaxf(st.m, mt);
   if (__builtin_amdgcn_ballot_w64(m_new > st.m) != 0) {
     const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((st.m - m_new) * scale);
     st.l *= alpha;
@@ -169,7 +172,7 @@ __device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, in
   qk_tile<DH>(sb, qf, sc);
   if (edge) mask_tile(sc, t0, key_lo, my_lim);
   bf16x8 pb[2][2];
-  softmax_update<DH, 2, false>(st, sc, pb, scale);
+  softmax_update<DH, 2, false, true>(st, sc, pb, scale);
   pv_tile<DH>(sb, pb, st);
   // the tile's probability sum on the matrix core: an all-ones A operand turns every
   // output row of 1 P^T into the column sums (the same bf16 P that multiplies V). Both
@@ -320,8 +323,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
     for (int j = 0; j < 16; ++j) st.o[db][j] = 0.f;
 
   // ---- per-lane sources of the tile DMA (slots beyond the filled length hold zeros) ----
-  const char* kbase = (const char*)(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride);
-  const char* vbase = (const char*)(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride);
+  // K [cap][dh] and V^T [dh][cap] of this (segment, head) as buffer resources
+  const __amdgpu_buffer_rsrc_t krs =
+      buffer_rsrc(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride, (uint32_t)p.kv_cap * KROW);
+  const __amdgpu_buffer_rsrc_t vrs =
+      buffer_rsrc(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride, (uint32_t)p.kv_cap * DH * 2);
   uint32_t k_off[K_INSTR], v_off[V_INSTR];  // per-lane byte offsets from the uniform tile base
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
@@ -339,10 +345,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
     char* sb = smem + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < K_INSTR; ++i)
-      dma16(kbase + (long)t0 * KROW + k_off[i], (lds_void*)(sb + (wave * K_INSTR + i) * 1024));
+      dma16_buf(krs, k_off[i], (uint32_t)t0 * KROW, (lds_void*)(sb + (wave * K_INSTR + i) * 1024));
 #pragma unroll
     for (int i = 0; i < V_INSTR; ++i)
-      dma16(vbase + (long)t0 * 2 + v_off[i], (lds_void*)(sb + K_BYTES + (wave * V_INSTR + i) * 1024));
+      dma16_buf(vrs, v_off[i], (uint32_t)t0 * 2, (lds_void*)(sb + K_BYTES + (wave * V_INSTR + i) * 1024));
   };
 
   constexpr bool EARLY_G = NW <= 2;
@@ -433,8 +439,11 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     for (int j = 0; j < 16; ++j) st.o[db][j] = 0.f;
 
   // ---- per-lane sources of the tile DMA (slots beyond the filled length hold zeros) ----
-  const char* kbase = (const char*)(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride);
-  const char* vbase = (const char*)(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride);
+  // K [cap][dh] and V^T [dh][cap] of this (segment, head) as buffer resources
+  const __amdgpu_buffer_rsrc_t krs =
+      buffer_rsrc(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride, (uint32_t)p.kv_cap * KROW);
+  const __amdgpu_buffer_rsrc_t vrs =
+      buffer_rsrc(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride, (uint32_t)p.kv_cap * DH * 2);
   uint32_t k_off[K_INSTR], v_off[V_INSTR];
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
@@ -464,13 +473,13 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     char* sb = kring + slot * K_BYTES;
 #pragma unroll
     for (int i = 0; i < K_INSTR; ++i)
-      dma16(kbase + (long)(t_first + j * KT) * KROW + k_off[i], (lds_void*)(sb + (wave * K_INSTR + i) * 1024));
+      dma16_buf(krs, k_off[i], (uint32_t)(t_first + j * KT) * KROW, (lds_void*)(sb + (wave * K_INSTR + i) * 1024));
   };
   auto issue_v = [&](int j, int slot) {
     char* sb = vring + slot * V_BYTES;
 #pragma unroll
     for (int i = 0; i < V_INSTR; ++i)
-      dma16(vbase + (long)(t_first + j * KT) * 2 + v_off[i], (lds_void*)(sb + (wave * V_INSTR + i) * 1024));
+      dma16_buf(vrs, v_off[i], (uint32_t)(t_first + j * KT) * 2, (lds_void*)(sb + (wave * V_INSTR + i) * 1024));
   };
   // per-lane parts of the fragment addresses (the slot adds a constant)
   const int pl = key_perm(l32);  // score row order: see qk_tile
@@ -515,9 +524,32 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   // rescale of O to the first tile.
   const float scale = p.scale_log2;
   const float tau = 8.f / scale;
+  // per-lane loop state derived from st.m, recomputed only when it moves: the exponent
+  // offset -m * scale (0 while no key was seen) and the threshold m + tau
+  float msub = 0.f, thr = -INFINITY;
+  auto tile_max = [&](const f32x16& v) { return max_halves(vmax16(v)); };
+  // move the reference of the lanes whose tile max passed the threshold (call under a
+  // wave-uniform branch) and rescale their running sum and O
+  auto raise_ref = [&](float mt) {
+    const bool up = mt > thr;
+    const float alpha = up ? __builtin_amdgcn_exp2f((st.m - mt) * scale) : 1.f;
+    if (up) {
+      st.m = mt;
+      msub = -mt * scale;
+      thr = mt + tau;
+    }
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[db][j] *= alpha;
+  };
   f32x16 sc;
   if (ntiles > 0) {
-    wait_vmcnt<0>();
+    // only K(0) is needed here: leave the loads issued after it in flight
+    if (ntiles > 2) wait_vmcnt<2 * PER_TILE>();        // K(1), V(0), K(2), V(1)
+    else if (ntiles == 2) wait_vmcnt<K_INSTR + 2 * V_INSTR>();  // K(1), V(0), V(1)
+    else wait_vmcnt<V_INSTR>();                         // V(0)
     lds_barrier();
     scores(0, sc);
   }
@@ -543,21 +575,8 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
         if (slot < key_lo || slot >= my_lim) sc[j] = -INFINITY;
       }
     }
-    float mt = sc[0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sc[j]);
-    mt = fmaxf(mt, other_half(mt));
-    if (__builtin_amdgcn_ballot_w64(mt > st.m + tau) != 0) {
-      const bool up = mt > st.m + tau;
-      const float alpha = up ? __builtin_amdgcn_exp2f((st.m - mt) * scale) : 1.f;
-      if (up) st.m = mt;
-      st.l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) st.o[db][j] *= alpha;
-    }
-    const float msub = st.m == -INFINITY ? 0.f : -st.m * scale;
+    const float mt = tile_max(sc);
+    if (__builtin_amdgcn_ballot_w64(mt > thr) != 0) raise_ref(mt);
     bf16x8 pb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -595,11 +614,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     bf16x8 kf[DH / 16], vf[2 * (DH / 32)];
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) kf[s] = *(const bf16x8*)(kb + k_frag[s]);
-    float mt = sc[0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sc[j]);
-    mt = fmaxf(mt, other_half(mt));
-    const float msub = st.m == -INFINITY ? 0.f : -st.m * scale;
+    const float mt = tile_max(sc);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 sn;
 #pragma unroll
@@ -619,20 +634,12 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     // keep the exponentials here, under the score MFMAs (the compiler would otherwise sink
     // them past the branch below)
     asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
-    if (__builtin_amdgcn_ballot_w64(mt > st.m + tau) != 0) {
-      const bool up = mt > st.m + tau;
-      const float alpha = up ? __builtin_amdgcn_exp2f((st.m - mt) * scale) : 1.f;
-      if (up) st.m = mt;
-      st.l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) st.o[db][j] *= alpha;
-      const float msub2 = -st.m * scale;
+    if (__builtin_amdgcn_ballot_w64(mt > thr) != 0) {
+      raise_ref(mt);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[8 * c + i], scale, msub2));
+        for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[8 * c + i], scale, msub));
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -829,8 +836,10 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   const int n_my = wave < ntiles ? (ntiles - wave + KS - 1) / KS : 0;
   OutRow<DH> orow;  // wave 0 writes the merged rows
   if (wave == 0 && q_ok) out_row_load<DH, true>(p, seg, h, qi, orow);
-  const char* kbase = (const char*)(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride);
-  const char* vbase = (const char*)(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride);
+  const __amdgpu_buffer_rsrc_t krs =
+      buffer_rsrc(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride, (uint32_t)p.kv_cap * KROW);
+  const __amdgpu_buffer_rsrc_t vrs =
+      buffer_rsrc(p.vt + seg * p.kv_seg_stride + h * p.kv_head_stride, (uint32_t)p.kv_cap * DH * 2);
   char* ring = smem + wave * 2 * STAGE;
   auto issue = [&](int j) {
     const int t0 = t_first + (wave + j * KS) * KT;
@@ -839,13 +848,13 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
     for (int i = 0; i < K_INSTR; ++i) {
       const int r = i * KRPI + lane / KCH, c = lane % KCH;
       const int cs = KCH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
-      dma16(kbase + (long)(t0 + r) * KROW + cs * 16, (lds_void*)(sb + i * 1024));
+      dma16_buf(krs, (uint32_t)(r * KROW + cs * 16), (uint32_t)t0 * KROW, (lds_void*)(sb + i * 1024));
     }
 #pragma unroll
     for (int i = 0; i < V_INSTR; ++i) {
       const int r = i * 8 + (lane >> 3);  // dh row
-      dma16(vbase + ((long)r * p.kv_cap + t0) * 2 + ((((lane & 7) ^ ((r >> 1) & 7))) << 4),
-            (lds_void*)(sb + K_BYTES + i * 1024));
+      dma16_buf(vrs, (uint32_t)r * (uint32_t)p.kv_cap * 2u + ((((lane & 7) ^ ((r >> 1) & 7))) << 4),
+                (uint32_t)t0 * 2, (lds_void*)(sb + K_BYTES + i * 1024));
     }
   };
   if (n_my > 0) issue(0);

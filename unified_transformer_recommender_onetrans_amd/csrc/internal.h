@@ -30,12 +30,22 @@ __device__ __forceinline__ float gelu_as(float x) {
   return fmaf(-(a * (q * t)), e, fmaxf(x, 0.0f));
 }
 
-// The value that lane l ^ 32 holds (v_permlane32_swap: no LDS traffic). Both lanes of a
-// pair must be active.
-__device__ __forceinline__ float other_half(float v) {
+// v_permlane32_swap of v with a copy of itself: lo holds the low half's values in both
+// halves, hi the high half's. (The elements are copied out before the bit casts: a
+// __builtin_bit_cast of a vector element reads element 0 with this compiler.)
+__device__ __forceinline__ void swap_halves(float v, float& lo, float& hi) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+  const uint32_t a = r[0], b = r[1];
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+
+// The value that lane l ^ 32 holds (no LDS traffic). Both lanes of a pair must be active.
+__device__ __forceinline__ float other_half(float v) {
+  float lo, hi;
+  swap_halves(v, lo, hi);
+  return (threadIdx.x & 32) ? lo : hi;
 }
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
@@ -45,6 +55,50 @@ __device__ __forceinline__ void dma16(const void* g, lds_void* l) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 #endif
+}
+
+// The same 16-byte DMA through a buffer resource: the address is the resource's base +
+// soff (wave-uniform, an SGPR) + voff (per lane), so no 64-bit address arithmetic per
+// lane; reads at or past the resource's byte count return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, lds_void* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+#endif
+}
+
+// Maxima as plain v_max instructions. The builtin fmaxf of values the compiler cannot
+// prove quiet (matrix-core results) first canonicalises each input with an extra
+// instruction; scores are never signalling NaNs.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// the max of 16 values (v[0] .. v[15]): seven v_max3 and one v_max in one block
+template <class V>
+__device__ __forceinline__ float vmax16(const V& v) {
+  float m;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max3_f32 %0, %0, %10, %11\n\t"
+      "v_max3_f32 %0, %0, %12, %13\n\t"
+      "v_max3_f32 %0, %0, %14, %15\n\t"
+      "v_max_f32 %0, %0, %16"
+      : "=&v"(m)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]),
+        "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+  return m;
+}
+// max(v, value of lane l ^ 32) in every lane
+__device__ __forceinline__ float max_halves(float v) {
+  float lo, hi;
+  swap_halves(v, lo, hi);
+  return vmax(lo, hi);
 }
 
 // Row addressing shared by the GEMM prologue/epilogue.
