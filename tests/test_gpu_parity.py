@@ -188,6 +188,51 @@ def test_peaked_attention_moves_softmax_reference():
     assert_close(ns_out[0, 0, 0].cpu().numpy(), ref_n[0, 0, 0], wl.ns_wdtype, "NS row of the peaked query")
 
 
+def test_peaked_many_user_prefill_moves_softmax_reference():
+    """The many-user prefill's tile kernel (attn_kernel<64, 4>) with keys far above the first
+    key tile's scores: with W_Q = W_K = I on the S side and every user's later events
+    repeating one token, the lazy softmax reference of the S queries has to move in the
+    middle of the key stream, and the S tails must still match the oracle."""
+    from unified_transformer_recommender_onetrans_amd import OneTrans
+    from unified_transformer_recommender_onetrans_amd._capi import lib
+    wl = Workload(name="peak_many", n_layers=2, d_model=128, n_heads=2, ffn_hidden=256, s_len=2048,
+                  q_sched=(2048, 1000), n_ns=4, n_users=16, n_candidates=2)
+    assert lib().onetrans_attention_route(0, 64, 2048, 2, 16).decode() == "attn_kernel<64,4>"
+    raw, _ = weights(wl)
+    raw = [dict(lw) for lw in raw]
+    d = wl.d_model
+    eye = np.eye(d, dtype=np.float32)
+    for lw in raw:
+        sq = lw["s_wqkv"].copy()
+        sq[:d], sq[d:2 * d] = eye, eye
+        lw["s_wqkv"] = sq
+    lay = O.layers_from_arrays(raw)
+    lens = _many_lens(wl)
+    s, lens, ns = _inputs(wl, lens)
+    for u in range(wl.n_users):
+        first = wl.s_len - int(lens[u])
+        if lens[u] > 128:
+            s[u, first + 128:] = s[u, first + 128]  # events from the 129th on repeat that one
+    # the premise, from the oracle's layer-0 quantities: for user 0's last S query the best
+    # key beats the best key of the first 64-key tile by more than 8 in log2 units
+    W = lay[0]
+    x0 = O.rmsnorm(np.asarray(s[0], np.float64), W.s_ga, EPS)
+    qS, kS = x0 @ W.s_wq.T, x0 @ W.s_wk.T
+    dh = d // wl.n_heads
+    for h in range(wl.n_heads):
+        sl = slice(h * dh, (h + 1) * dh)
+        logits = kS[:, sl] @ qS[-1, sl] / np.sqrt(dh)
+        assert (logits.max() - logits[:64].max()) * np.log2(np.e) > 8.5
+    m = OneTrans(config(wl), device_weights(raw))
+    cache = m.new_cache(wl.n_users)
+    s_out = m.user_prefill(bf16_dev(s), torch.from_numpy(lens).cuda(), cache)
+    torch.cuda.synchronize()
+    s_out = s_out.cpu().numpy()
+    for u in range(wl.n_users):
+        _, ot = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[u], int(lens[u]))
+        assert_close(s_out[u], ot, wl.ns_wdtype, f"user {u} (len {lens[u]}) S tail")
+
+
 # user-side NS rows: (workload, histories, n_ns_user)
 USER_NS = {
     "b_dh64_P32_u8": (SMALL["b_dh64_P32"][0], [200, 1], 8),
