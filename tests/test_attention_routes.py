@@ -13,7 +13,7 @@ from unified_transformer_recommender_onetrans_amd import _capi as C
 
 ALL_ROUTES = {
     "attn_ns2_kernel<64,2>", "attn_ns2_kernel<64,1>", "attn_ns2_kernel<32,2>", "attn_ns2_kernel<32,1>",
-    "attn_split_kernel<64,4,true>", "attn_split_kernel<32,4,true>", "attn_split_kernel<64,4,false>",
+    "attn_split_kernel<64,5,true>", "attn_split_kernel<32,4,true>", "attn_split_kernel<64,5,false>",
     "attn_split_kernel<32,4,false>", "attn_kernel<64,4>", "attn_kernel<32,4>", "attn_kernel<64,2>",
     "attn_kernel<32,2>",
 }
@@ -38,7 +38,7 @@ def prefill_routes(lib, wl, B):
 def test_dispatch_thresholds(lib):
     # 32 queries per block; S: < 1024 blocks split the keys, >= 2048 four blocks share a
     # workgroup, in between two; NS: >= 1024 blocks two query blocks per workgroup
-    assert route(lib, False, 64, 32 * 511, 2, 1) == "attn_split_kernel<64,4,false>"
+    assert route(lib, False, 64, 32 * 511, 2, 1) == "attn_split_kernel<64,5,false>"
     assert route(lib, False, 64, 32 * 256, 2, 2) == "attn_kernel<64,2>"
     assert route(lib, False, 64, 32 * 1023, 2, 1) == "attn_kernel<64,2>"
     assert route(lib, False, 64, 32 * 1024, 2, 1) == "attn_kernel<64,4>"

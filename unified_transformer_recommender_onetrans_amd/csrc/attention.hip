@@ -938,8 +938,9 @@ void launch_attn_nw(const AttnParams& p, int n_seg, hipStream_t s) {
 // Which kernel instance runs a launch: 32 queries per wave, a workgroup's waves share the
 // K/V tiles. NS: each tile's keys split over two waves per query block, 2 query blocks (4
 // waves) per workgroup when there are blocks for 512 such workgroups, else 1. S: with few
-// query blocks (one user's prefill, appends) each block's keys are split over four waves,
-// the blocks of one (user, head) grouped on one XCD when there are several users; with many
+// query blocks (one user's prefill, appends) each block's keys are split over five waves
+// (head dim 64: their double-buffered tile rings fill the 160 KB of LDS; four for head dim
+// 32), the blocks of one (user, head) grouped on one XCD when there are several users; with many
 // (a batch of users' prefill) 4 or 2 query blocks share a workgroup's key stream. The K/V of
 // a layer is L2-resident, so streaming it to more workgroups is cheap.
 AttnRoute attention_route(bool ns, int dh, int nq, int H, int n_seg) {
@@ -963,9 +964,9 @@ const char* attention_route_name(AttnRoute r) {
     case ATTN_NS2_64_1: return "attn_ns2_kernel<64,1>";
     case ATTN_NS2_32_2: return "attn_ns2_kernel<32,2>";
     case ATTN_NS2_32_1: return "attn_ns2_kernel<32,1>";
-    case ATTN_SPLIT_64_GROUPED: return "attn_split_kernel<64,4,true>";
+    case ATTN_SPLIT_64_GROUPED: return "attn_split_kernel<64,5,true>";
     case ATTN_SPLIT_32_GROUPED: return "attn_split_kernel<32,4,true>";
-    case ATTN_SPLIT_64: return "attn_split_kernel<64,4,false>";
+    case ATTN_SPLIT_64: return "attn_split_kernel<64,5,false>";
     case ATTN_SPLIT_32: return "attn_split_kernel<32,4,false>";
     case ATTN_TILE_64_4: return "attn_kernel<64,4>";
     case ATTN_TILE_32_4: return "attn_kernel<32,4>";
@@ -987,12 +988,12 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
     case ATTN_NS2_32_2: launch_attn_ns2<32, 2>(p, n_seg, s); break;
     case ATTN_NS2_32_1: launch_attn_ns2<32, 1>(p, n_seg, s); break;
     case ATTN_SPLIT_64_GROUPED:
-      hipLaunchKernelGGL((attn_split_kernel<64, 4, true>), grouped_grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((attn_split_kernel<64, 5, true>), grouped_grid, dim3(320), 0, s, p);
       break;
     case ATTN_SPLIT_32_GROUPED:
       hipLaunchKernelGGL((attn_split_kernel<32, 4, true>), grouped_grid, dim3(256), 0, s, p);
       break;
-    case ATTN_SPLIT_64: hipLaunchKernelGGL((attn_split_kernel<64, 4, false>), split_grid, dim3(256), 0, s, p); break;
+    case ATTN_SPLIT_64: hipLaunchKernelGGL((attn_split_kernel<64, 5, false>), split_grid, dim3(320), 0, s, p); break;
     case ATTN_SPLIT_32: hipLaunchKernelGGL((attn_split_kernel<32, 4, false>), split_grid, dim3(256), 0, s, p); break;
     case ATTN_TILE_64_4: launch_attn_nw<64, 4>(p, n_seg, s); break;
     case ATTN_TILE_32_4: launch_attn_nw<32, 4>(p, n_seg, s); break;
