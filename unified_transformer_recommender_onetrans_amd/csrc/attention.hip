@@ -681,6 +681,9 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
   if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
 
+  // the output row's residual and gains, loaded under the own-key phase and the merge
+  OutRow<DH> orow;
+  if (kh == 0 && q_ok) out_row_load<DH, false>(p, seg, h, qi, orow);
   if (kh == 0 && wave_live) {
     // 32 keys [t0, t0 + 32) of a row-major K / V block (rows past n_rows - 1 are read as
     // that row and masked), visible to this lane when vis(key) holds
@@ -748,8 +751,6 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   }
   __syncthreads();
   if (kh == 1 || !q_ok) return;
-  OutRow<DH> orow;
-  out_row_load<DH, true>(p, seg, h, qi, orow);
   const float m1 = mw[lane], l1 = mw[64 + lane];
   const float m = fmaxf(st.m, m1);
   const float f0 = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - m) * p.scale_log2);
@@ -760,7 +761,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) st.o[db][j] = st.o[db][j] * f0 + mw[128 + (db * 16 + j) * 64 + lane] * f1;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  out_row_store<DH, true>(p, seg, h, qi, orow, st.o, inv);
+  out_row_store<DH, false>(p, seg, h, qi, orow, st.o, inv);
 }
 
 // S-token attention with the keys of one 32-query block split over KS waves: wave w takes
