@@ -148,6 +148,45 @@ def test_many_user_prefill_tile_kernels(name):
                          f"user {u} scores after the append")
 
 
+# appends to many users with several query blocks per (user, head) in the S attention (the
+# split kernel with the blocks of a (user, head) grouped on one XCD); 80 new events leave
+# a ragged block
+MANY_APPENDS = {
+    "k_dh32_64users_m80": (Workload(name="k", n_layers=2, d_model=64, n_heads=2, ffn_hidden=128, s_len=300,
+                                    q_sched=(300, 150), n_ns=4, n_users=64, n_candidates=2), 80),
+    "l_dh64_64users_m96": (Workload(name="l", n_layers=2, d_model=128, n_heads=2, ffn_hidden=256, s_len=300,
+                                    q_sched=(300, 97), n_ns=4, n_users=64, n_candidates=2), 96),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY_APPENDS))
+def test_many_user_append_several_query_blocks(name):
+    from unified_transformer_recommender_onetrans_amd._capi import lib
+    wl, m = MANY_APPENDS[name]
+    B = wl.n_users
+    assert lib().onetrans_attention_route(0, wl.head_dim, m, wl.n_heads, B).decode().endswith(",true>")
+    print(f"case {name}: B={B} m={m}", flush=True)
+    mdl, lay = model(wl, append_cap=m)
+    base = [300, 0, 1, 33, 64, 65, 127, 128, 129, 200, 255, 256, 257, 299]
+    lens = [base[u % len(base)] for u in range(B)]
+    s, lens, ns = _inputs(wl, lens)
+    sd, ld, nd = _dev(s, lens, ns)
+    cache = mdl.new_cache(B)
+    mdl.user_prefill(sd, ld, cache)
+    new = make_append_tokens(wl, m=m)
+    app = mdl.kv_append(bf16_dev(new), cache)
+    scored = {u: mdl.score_candidates(cache, u, nd[u]) for u in (0, 1, B - 1)}
+    torch.cuda.synchronize()
+    app = app.cpu().numpy()
+    for u in range(B):
+        oc, _ = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[u], int(lens[u]))
+        oc, oa = O.append(lay, wl.n_heads, EPS, oc, new[u])
+        assert_close(app[u], oa, wl.ns_wdtype, f"user {u} (len {lens[u]}) appended rows")
+        if u in scored:
+            assert_close(scored[u].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, ns[u]), wl.ns_wdtype,
+                         f"user {u} scores after the append")
+
+
 def test_peaked_attention_moves_softmax_reference():
     """Cached keys far above the first key tile's scores: the NS kernel's online softmax
     has to move its reference maximum in the middle of the key stream (its rescale
