@@ -148,6 +148,21 @@ def test_many_user_prefill_tile_kernels(name):
                          f"user {u} scores after the append")
 
 
+def test_one_tile_per_workgroup_gemms():
+    """160 candidates x 48 NS positions at d = 192, F = 768: the NS QKV (N = 576) and FFN up
+    (N = 768) GEMMs take one 256x192 tile per workgroup (the smaller tiles would need three
+    rounds of the chip), with 96 padding rows in every tile; every output is compared."""
+    wl = Workload(name="t256", n_layers=2, d_model=192, n_heads=3, ffn_hidden=768, s_len=200,
+                  q_sched=(200, 64), n_ns=48, n_users=1, n_candidates=160)
+    m, lay = model(wl)
+    s, lens, ns = _inputs(wl, [170])
+    s_out, ns_out = m.block_forward(*_dev(s, lens, ns))
+    torch.cuda.synchronize()
+    ref_t, ref_n = O.block_forward(lay, wl.q_sched, wl.n_heads, EPS, s, lens, ns)
+    assert_close(s_out.cpu().numpy(), ref_t, wl.ns_wdtype, "S tail")
+    assert_close(ns_out.cpu().numpy(), ref_n, wl.ns_wdtype, "NS out")
+
+
 # appends to many users with several query blocks per (user, head) in the S attention (the
 # split kernel with the blocks of a (user, head) grouped on one XCD); 80 new events leave
 # a ragged block

@@ -218,6 +218,115 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
   }
 }
 
+// One 256x192 output tile per workgroup (no persistence), for launches whose tiles all fit
+// on the chip at once: fewer operand bytes per CU than two or three smaller tiles (each
+// weight row is fetched once per 256 rows, each activation row once per 192 columns).
+// With one tile per workgroup no epilogue store ever precedes a k-tile wait, so all 8
+// waves both stream operands and compute (a 4 x 2 grid of 64x96 parts, 96 accumulators
+// per lane at two waves per SIMD). k-tiles are 32 wide (64-byte LDS rows) so that the
+// ring holds 5 stages; each k-tile is 28 DMA instructions of 1 KB: 2 of A per wave, 2 of
+// B for waves 0-3 and 1 for waves 4-7.
+template <int KIND, int SIDE>
+__global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int n_tiles_n) {
+  constexpr int BM = 256, BN = 192, BK = 32, STAGES = 5;
+  constexpr int WN = 2, TM = 64, TN = 96, MI = TM / 32, NI = TN / 32;
+  constexpr int ROW = BK * 2;  // bytes per LDS row (fp16)
+  constexpr int A_BYTES = BM * ROW, STAGE = (BM + BN) * ROW;
+  constexpr int RPI = 1024 / ROW, CPR = ROW / 16;  // rows per DMA instruction, chunks per row
+  static_assert(STAGES * STAGE <= 159 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const RowMap rm = p.rm;
+  const int M = p.M, N = p.N, K = p.K;
+  const float inv_rps = 1.0f / (float)rm.rows_per_seg;
+  const int nk = K / BK;
+  // tile of this workgroup: each XCD (workgroup L runs on XCD L % 8) takes a contiguous range
+  // of tiles, the N index fastest, so the tiles of one activation block share that XCD's L2
+  const int total = gridDim.x, L = blockIdx.x;
+  const int x = L % N_XCD, w = x * (total / N_XCD) + min(x, total % N_XCD) + L / N_XCD;
+  const int nt = w % n_tiles_n, g = w / n_tiles_n;  // one M tile per group (M <= 256)
+  const int n0 = nt * BN;
+
+  // per-lane DMA sources: A instructions 2w, 2w+1; B instructions 2w, 2w+1 (w < 4) or 4+w
+  const char* a_src[2];
+  const char* b_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (2 * wave + i) * RPI + lane / CPR;
+    const int row = min(r, M - 1);
+    int seg, tt;
+    split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
+    a_src[i] = (const char*)(p.a_in + hid_row(rm, seg, tt, g) * (long)K) + (swz<ROW>(lane % CPR, r) << 4);
+  }
+  const char* wbase = (const char*)p.w + (long)g * p.w_group_stride * 2;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int bi = wave < 4 ? 2 * wave + i : 4 + wave;
+    const int r = bi * RPI + lane / CPR;
+    b_src[i] = wbase + (long)(n0 + r) * K * 2 + (swz<ROW>(lane % CPR, r) << 4);
+  }
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % STAGES) * STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(a_src[i] + kt * ROW, (lds_void*)(st + (2 * wave + i) * 1024));
+    if (wave < 4) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(b_src[i] + kt * ROW, (lds_void*)(st + A_BYTES + (2 * wave + i) * 1024));
+    } else {
+      dma16(b_src[0] + kt * ROW, (lds_void*)(st + A_BYTES + (4 + wave) * 1024));
+    }
+  };
+  // this wave's part of k-tile kt is in LDS (later tiles of this wave may stay in flight)
+  auto wait_kt = [&](int later) {
+    if (wave < 4) wait_tiles<4, STAGES - 2>(later);
+    else wait_tiles<3, STAGES - 2>(later);
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
+  TilePre<KIND, MI, NI> pre;
+  tile_prefetch<KIND, MI, NI, TM, TN>(p, 0, n0, g, wm, wn, pre);
+
+  for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_kt(min(STAGES - 2, nk - 1 - kt));
+    lds_barrier();  // k-tile kt is in for everyone; everyone is done with kt - 1, whose slot refills now
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const char* st = smem + (kt % STAGES) * STAGE;
+    f16x8 af[2][MI], bf[2][NI];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int r = wm * TM + mi * 32 + (lane & 31);
+        af[ks][mi] = *(const f16x8*)(st + r * ROW + (swz<ROW>(c, r) << 4));
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int r = wn * TN + ni * 32 + (lane & 31);
+        bf[ks][ni] = *(const f16x8*)(st + A_BYTES + r * ROW + (swz<ROW>(c, r) << 4));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[ks][ni], af[ks][mi], acc[mi][ni], 0, 0, 0);
+  }
+  tile_epilogue<KIND, false, MI, NI, TM, TN>(p, acc, 0, n0, g, wm, wn, pre);
+}
+
 // Tile shapes: (BM, BN, compute waves along M). 96-wide tiles are fp16-only (a 96-row E4M3
 // tile is not a whole number of 4 KB DMA rounds). The operand ring takes up to 159 KB of
 // LDS, at most 8 stages.
@@ -272,6 +381,16 @@ void launch_kind(bool fp8, const GemmParams& p, hipStream_t s) {
     if (!fits(cands[i].bn)) continue;
     const double c = tile_cost(p, fp8, cands[i].bm, cands[i].bn);
     if (best < 0 || c < best_cost) { best = i; best_cost = c; }
+  }
+  // one 256x192 tile per workgroup (fp16 weights, every tile on the chip at once) when the
+  // same cost model prefers it
+  if constexpr (KD != GEMM_FFN_DOWN) {
+    if (!fp8 && p.M <= 256 && fits(192) && (long)(p.N / 192) * p.groups <= 256 &&
+        tile_cost(p, false, 256, 192) < best_cost) {
+      const int tn = p.N / 192;
+      hipLaunchKernelGGL((gemm_tile256_kernel<KD, SIDE>), dim3(tn * p.groups), dim3(512), 0, s, p, tn);
+      return;
+    }
   }
   switch (best) {
     case 0: launch_cfg<KD, SIDE, 128, 96, 4>(fp8, p, s); break;
