@@ -146,8 +146,9 @@ int onetrans_check_config(const onetrans_config* cfg);
 size_t onetrans_packed_weight_bytes(const onetrans_config* cfg);
 
 /* Converts the caller's per-layer weights (layers[cfg->n_layers]) into the
- * packed device buffer `packed` (bf16 weights become fp16, E4M3FN codes and
- * fp32 gains/scales are copied). Asynchronous on `stream`. The packed buffer
+ * packed device buffer `packed` (bf16 weights become fp16, E4M3FN codes are
+ * copied, both rearranged into the GEMMs' blocked layout; fp32 gains/scales are
+ * copied). Asynchronous on `stream`. The packed buffer
  * must stay alive and unchanged while compute calls use it.
  * Range: the bf16 -> fp16 conversion (round to nearest even) is exact for weights
  * with 2^-17 <= |w| < 65536 (the largest such bf16 value is 65280) and for zero; smaller magnitudes are rounded to the

@@ -23,6 +23,36 @@ __global__ void bf16_to_f16_kernel(const uint16_t* __restrict__ src, _Float16* _
   }
 }
 
+// Weight matrices [G][N][K] (row n = output column of the linear map) into panels
+// [G][N/32][K/64][32][64]: every 32-row, 64-wide block is one contiguous 4 KB (fp16) or
+// 2 KB (E4M3) run, so a GEMM k-tile of a weight tile reads whole contiguous blocks instead
+// of 64- or 128-byte pieces of rows K elements apart. bf16 becomes fp16 as in
+// bf16_to_f16_kernel; E4M3 codes are copied. One thread per 16 output bytes.
+template <bool FP8>
+__global__ void pack_panels_kernel(const void* __restrict__ src, void* __restrict__ dst, long n_chunks, int N, int K) {
+  constexpr int E = FP8 ? 16 : 8;  // elements per 16-byte chunk
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_chunks) return;
+  const long per_row = K / E, per_mat = (long)N * per_row;
+  const long g = i / per_mat, r = i - g * per_mat;
+  const int n = (int)(r / per_row), k = (int)(r - (long)n * per_row) * E;
+  const long si = g * (long)N * K + (long)n * K + k;
+  const long di = g * (long)N * K + ((long)(n >> 5) * (K >> 6) + (k >> 6)) * 2048 + (n & 31) * 64 + (k & 63);
+  if constexpr (FP8) {
+    *(uint4*)((uint8_t*)dst + di) = *(const uint4*)((const uint8_t*)src + si);
+  } else {
+    const uint4 v = *(const uint4*)((const uint16_t*)src + si);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    _Float16 o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = (_Float16)__builtin_bit_cast(float, w[j] << 16);
+      o[2 * j + 1] = (_Float16)__builtin_bit_cast(float, w[j] & 0xFFFF0000u);
+    }
+    *(uint4*)((_Float16*)dst + di) = *(const uint4*)o;
+  }
+}
+
 // One wave per input row: bf16 -> fp32 residual, the first norm's operand x * g (fp16) and
 // the row's sum of squares (slot 0). 8 elements per lane and chunk, d <= 1024.
 __global__ __launch_bounds__(256) void input_rows_kernel(InputParams p) {
@@ -105,6 +135,16 @@ hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, long n, hipStr
   if (n <= 0) return hipSuccess;
   const long threads = (n + 7) / 8;
   hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_panels(const void* src, void* dst, bool fp8, long G, int N, int K, hipStream_t s) {
+  if (G <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (N % 32 != 0 || K % 64 != 0) return hipErrorInvalidValue;
+  const long chunks = G * (long)N * K / (fp8 ? 16 : 8);
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  if (fp8) hipLaunchKernelGGL(pack_panels_kernel<true>, grid, dim3(256), 0, s, src, dst, chunks, N, K);
+  else hipLaunchKernelGGL(pack_panels_kernel<false>, grid, dim3(256), 0, s, src, dst, chunks, N, K);
   return hipGetLastError();
 }
 

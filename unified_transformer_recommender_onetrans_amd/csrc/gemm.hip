@@ -112,8 +112,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
 #pragma unroll
         for (int i = 0; i < B_INSTR; ++i) {
           const int r = (lw * B_INSTR + i) * B_RPI + lane / B_CPR;
-          const int n = min(n0 + r, N - 1);
-          b_src[i] = wbase + (long)n * K * (FP8 ? 1 : 2) + (swz<BROW>(lane % B_CPR, r) << 4);
+          const int n = n0 + r;  // N % BN == 0
+          b_src[i] = wbase + ((long)(n >> 5) * (K >> 6) * 2048 + (n & 31) * 64) * (FP8 ? 1 : 2) +
+                     (swz<BROW>(lane % B_CPR, r) << 4);
         }
       }
       char* st = smem + (s % STAGES) * STAGE;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
         dma16(a_src[i] + iss_kt * AROW, (lds_void*)(st + (lw * A_INSTR + i) * 1024));
 #pragma unroll
       for (int i = 0; i < B_INSTR; ++i)
-        dma16(b_src[i] + iss_kt * BROW, (lds_void*)(st + A_BYTES + (lw * B_INSTR + i) * 1024));
+        dma16(b_src[i] + iss_kt * (2048 * (FP8 ? 1 : 2)), (lds_void*)(st + A_BYTES + (lw * B_INSTR + i) * 1024));
       if (++iss_kt == nk) { iss_kt = 0; ++iss_t; }
     };
     int s_issue = 0;
@@ -264,17 +265,19 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
   for (int i = 0; i < 2; ++i) {
     const int bi = wave < 4 ? 2 * wave + i : 4 + wave;
     const int r = bi * RPI + lane / CPR;
-    b_src[i] = wbase + (long)(n0 + r) * K * 2 + (swz<ROW>(lane % CPR, r) << 4);
+    const int n = n0 + r;
+    b_src[i] = wbase + ((long)(n >> 5) * (K >> 6) * 2048 + (n & 31) * 64) * 2 + (swz<ROW>(lane % CPR, r) << 4);
   }
   auto issue = [&](int kt) {
     char* st = smem + (kt % STAGES) * STAGE;
+    const long boff = (long)(kt >> 1) * 4096 + (kt & 1) * ROW;  // 32-wide half of a 64-wide weight block
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(a_src[i] + kt * ROW, (lds_void*)(st + (2 * wave + i) * 1024));
     if (wave < 4) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(b_src[i] + kt * ROW, (lds_void*)(st + A_BYTES + (2 * wave + i) * 1024));
+      for (int i = 0; i < 2; ++i) dma16(b_src[i] + boff, (lds_void*)(st + A_BYTES + (2 * wave + i) * 1024));
     } else {
-      dma16(b_src[0] + kt * ROW, (lds_void*)(st + A_BYTES + (4 + wave) * 1024));
+      dma16(b_src[0] + boff, (lds_void*)(st + A_BYTES + (4 + wave) * 1024));
     }
   };
   // this wave's part of k-tile kt is in LDS (later tiles of this wave may stay in flight)

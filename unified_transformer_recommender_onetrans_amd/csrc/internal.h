@@ -227,6 +227,9 @@ hipError_t launch_input_rows(const InputParams& p, hipStream_t s);
 
 // Elementwise helpers.
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, long n, hipStream_t s);
+// G weight matrices [N][K] (bf16 -> fp16, or E4M3 codes) into the GEMMs' panel layout
+// [G][N/32][K/64][32][64]; N % 32 == 0 and K % 64 == 0.
+hipError_t launch_pack_panels(const void* src, void* dst, bool fp8, long G, int N, int K, hipStream_t s);
 hipError_t launch_copy_rows_f32(const float* src, long src_seg_stride, float* dst, long dst_seg_stride,
                                 long row_elems, int n_seg, hipStream_t s);
 hipError_t launch_cache_read(const __bf16* k, const __bf16* vt, int H, int dh, int cap, int rows,

@@ -654,20 +654,20 @@ int onetrans_pack_weights(const onetrans_config* cfg, const onetrans_layer_weigh
   for (int l = 0; l < s.L; ++l) {
     const onetrans_layer_weights& w = layers[l];
     const LayerOffsets& o = lo[l];
-    OT_HIP(launch_bf16_to_f16((const uint16_t*)w.s_wqkv, (_Float16*)(pk + o.s_wqkv), 3 * d * d, stream), "pack");
-    OT_HIP(launch_bf16_to_f16((const uint16_t*)w.s_w1, (_Float16*)(pk + o.s_w1), F * d, stream), "pack");
-    OT_HIP(launch_bf16_to_f16((const uint16_t*)w.s_w2, (_Float16*)(pk + o.s_w2), d * F, stream), "pack");
+    OT_HIP(launch_pack_panels(w.s_wqkv, pk + o.s_wqkv, false, 1, 3 * d, d, stream), "pack");
+    OT_HIP(launch_pack_panels(w.s_w1, pk + o.s_w1, false, 1, F, d, stream), "pack");
+    OT_HIP(launch_pack_panels(w.s_w2, pk + o.s_w2, false, 1, d, F, stream), "pack");
     OT_HIP(hipMemcpyAsync(pk + o.s_ga, w.s_g_attn, d * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
     OT_HIP(hipMemcpyAsync(pk + o.s_gf, w.s_g_ffn, d * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
     if (s.fp8) {
-      OT_HIP(hipMemcpyAsync(pk + o.ns_wqkv, w.ns_wqkv, P * 3 * d * d, hipMemcpyDeviceToDevice, stream), "pack copy");
-      OT_HIP(hipMemcpyAsync(pk + o.ns_w1, w.ns_w1, P * F * d, hipMemcpyDeviceToDevice, stream), "pack copy");
-      OT_HIP(hipMemcpyAsync(pk + o.ns_w2, w.ns_w2, P * d * F, hipMemcpyDeviceToDevice, stream), "pack copy");
+      OT_HIP(launch_pack_panels(w.ns_wqkv, pk + o.ns_wqkv, true, P, 3 * d, d, stream), "pack");
+      OT_HIP(launch_pack_panels(w.ns_w1, pk + o.ns_w1, true, P, F, d, stream), "pack");
+      OT_HIP(launch_pack_panels(w.ns_w2, pk + o.ns_w2, true, P, d, F, stream), "pack");
       OT_HIP(hipMemcpyAsync(pk + o.ns_scale, w.ns_scale, P * 5 * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
     } else {
-      OT_HIP(launch_bf16_to_f16((const uint16_t*)w.ns_wqkv, (_Float16*)(pk + o.ns_wqkv), P * 3 * d * d, stream), "pack");
-      OT_HIP(launch_bf16_to_f16((const uint16_t*)w.ns_w1, (_Float16*)(pk + o.ns_w1), P * F * d, stream), "pack");
-      OT_HIP(launch_bf16_to_f16((const uint16_t*)w.ns_w2, (_Float16*)(pk + o.ns_w2), P * d * F, stream), "pack");
+      OT_HIP(launch_pack_panels(w.ns_wqkv, pk + o.ns_wqkv, false, P, 3 * d, d, stream), "pack");
+      OT_HIP(launch_pack_panels(w.ns_w1, pk + o.ns_w1, false, P, F, d, stream), "pack");
+      OT_HIP(launch_pack_panels(w.ns_w2, pk + o.ns_w2, false, P, d, F, stream), "pack");
     }
     OT_HIP(hipMemcpyAsync(pk + o.ns_ga, w.ns_g_attn, P * d * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
     OT_HIP(hipMemcpyAsync(pk + o.ns_gf, w.ns_g_ffn, P * d * 4, hipMemcpyDeviceToDevice, stream), "pack copy");
