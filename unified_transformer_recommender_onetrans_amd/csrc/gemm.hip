@@ -224,12 +224,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
 // weight row is fetched once per 256 rows, each activation row once per 192 columns).
 // With one tile per workgroup no epilogue store ever precedes a k-tile wait, so all 8
 // waves both stream operands and compute (a 4 x 2 grid of 64x96 parts, 96 accumulators
-// per lane at two waves per SIMD). k-tiles are 32 wide (64-byte LDS rows) so that the
-// ring holds 5 stages; each k-tile is 28 DMA instructions of 1 KB: 2 of A per wave, 2 of
-// B for waves 0-3 and 1 for waves 4-7.
+// per lane at two waves per SIMD). k-tiles are 64 wide, so every row of a k-tile is one
+// whole 128-byte line (a weight k-tile is six contiguous 4 KB panel blocks); the 56 KB
+// stages leave room for a ring of two (the next k-tile streams while this one is
+// multiplied). Each k-tile is 56 DMA instructions of 1 KB, 4 of A and 3 of B per wave.
 template <int KIND, int SIDE>
 __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int n_tiles_n) {
-  constexpr int BM = 256, BN = 192, BK = 32, STAGES = 5;
+  constexpr int BM = 256, BN = 192, BK = 64, STAGES = 2;
   constexpr int WN = 2, TM = 64, TN = 96, MI = TM / 32, NI = TN / 32;
   constexpr int ROW = BK * 2;  // bytes per LDS row (fp16)
   constexpr int A_BYTES = BM * ROW, STAGE = (BM + BN) * ROW;
@@ -249,12 +250,12 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
   const int nt = w % n_tiles_n, g = w / n_tiles_n;  // one M tile per group (M <= 256)
   const int n0 = nt * BN;
 
-  // per-lane DMA sources: A instructions 2w, 2w+1; B instructions 2w, 2w+1 (w < 4) or 4+w
-  const char* a_src[2];
-  const char* b_src[2];
+  // per-lane DMA sources: A instructions 4w .. 4w+3, B instructions 3w .. 3w+2
+  const char* a_src[4];
+  const char* b_src[3];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (2 * wave + i) * RPI + lane / CPR;
+  for (int i = 0; i < 4; ++i) {
+    const int r = (4 * wave + i) * RPI + lane / CPR;
     const int row = min(r, M - 1);
     int seg, tt;
     split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
@@ -262,29 +263,21 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
   }
   const char* wbase = (const char*)p.w + (long)g * p.w_group_stride * 2;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int bi = wave < 4 ? 2 * wave + i : 4 + wave;
+  for (int i = 0; i < 3; ++i) {
+    const int bi = 3 * wave + i;
     const int r = bi * RPI + lane / CPR;
     const int n = n0 + r;
     b_src[i] = wbase + ((long)(n >> 5) * (K >> 6) * 2048 + (n & 31) * 64) * 2 + (swz<ROW>(lane % CPR, r) << 4);
   }
   auto issue = [&](int kt) {
     char* st = smem + (kt % STAGES) * STAGE;
-    const long boff = (long)(kt >> 1) * 4096 + (kt & 1) * ROW;  // 32-wide half of a 64-wide weight block
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(a_src[i] + kt * ROW, (lds_void*)(st + (2 * wave + i) * 1024));
-    if (wave < 4) {
+    for (int i = 0; i < 4; ++i) dma16(a_src[i] + kt * ROW, (lds_void*)(st + (4 * wave + i) * 1024));
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(b_src[i] + boff, (lds_void*)(st + A_BYTES + (2 * wave + i) * 1024));
-    } else {
-      dma16(b_src[0] + boff, (lds_void*)(st + A_BYTES + (4 + wave) * 1024));
-    }
+    for (int i = 0; i < 3; ++i) dma16(b_src[i] + (long)kt * 4096, (lds_void*)(st + A_BYTES + (3 * wave + i) * 1024));
   };
-  // this wave's part of k-tile kt is in LDS (later tiles of this wave may stay in flight)
-  auto wait_kt = [&](int later) {
-    if (wave < 4) wait_tiles<4, STAGES - 2>(later);
-    else wait_tiles<3, STAGES - 2>(later);
-  };
+  // this wave's part of k-tile kt is in LDS
+  auto wait_kt = [&](int later) { wait_tiles<7, STAGES - 2>(later); };
 
   const int wm = wave / WN, wn = wave % WN;
   f32x16 acc[MI][NI];
@@ -304,9 +297,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
     lds_barrier();  // k-tile kt is in for everyone; everyone is done with kt - 1, whose slot refills now
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     const char* st = smem + (kt % STAGES) * STAGE;
-    f16x8 af[2][MI], bf[2][NI];
+    f16x8 af[4][MI], bf[4][NI];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
       const int c = 2 * ks + (lane >> 5);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
@@ -320,7 +313,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
