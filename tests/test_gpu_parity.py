@@ -163,6 +163,24 @@ def test_one_tile_per_workgroup_gemms():
     assert_close(ns_out.cpu().numpy(), ref_n, wl.ns_wdtype, "NS out")
 
 
+@pytest.mark.parametrize("wdtype", ["bf16", "e4m3"])
+def test_persistent_eight_wave_gemms(wdtype):
+    """2048 candidates x 16 NS positions at d = 192, F = 384: the NS QKV (N = 576) and FFN up
+    (N = 384) GEMMs take 256x192 tiles on the persistent kernel with eight compute waves
+    (several tiles per workgroup, M > 256); every output is compared."""
+    wl = Workload(name="p8", n_layers=2, d_model=192, n_heads=3, ffn_hidden=384, s_len=160,
+                  q_sched=(160, 40), n_ns=16, n_users=1, n_candidates=2048, ns_wdtype=wdtype)
+    m, lay = model(wl)
+    s, lens, ns = _inputs(wl, [150])
+    sd, ld, nd = _dev(s, lens, ns)
+    cache = m.new_cache(1)
+    m.user_prefill(sd, ld, cache)
+    got = m.score_candidates(cache, 0, nd[0])
+    torch.cuda.synchronize()
+    oc, _ = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[0], int(lens[0]))
+    assert_close(got.cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, ns[0]), wdtype, "NS rows")
+
+
 # appends to many users with several query blocks per (user, head) in the S attention (the
 # split kernel with the blocks of a (user, head) grouped on one XCD); 80 new events leave
 # a ragged block

@@ -12,7 +12,7 @@
 //                   partial sums of squares (the deferred RMSNorm described with NormOut)
 // A group is one NS position (private weights) or the shared S weights.
 //
-// Persistent schedule, one workgroup of 8 waves per CU. The work list (BM x BN
+// Persistent schedule, one workgroup of 8 or 12 waves per CU. The work list (BM x BN
 // output tiles of every group) is split into 8 contiguous ranges, one per XCD
 // (the hardware dispatches block L to XCD L % 8), and each XCD's workgroups take
 // its items round-robin, so neighbouring tiles that share weight rows and
@@ -20,12 +20,13 @@
 //
 // Warp specialisation. Loads and stores share one vmcnt counter on gfx9, so a
 // wave that both streams operands and writes results must wait for its own
-// stores whenever it waits for a k-tile. Here waves 4-7 only stream: they issue
-// the k-tiles (global -> LDS with global_load_lds_dwordx4, 16 bytes per lane),
-// wait for them and meet the compute waves at one barrier per k-tile. Waves 0-3
-// only compute: MFMA from LDS, then the epilogue's stores, which drain in the
-// background while the loaders keep up to STAGES-1 k-tiles of the next item in
-// flight. The ring holds 3-8 stages (about 128-144 KB of LDS).
+// stores whenever it waits for a k-tile. Here the last four waves only stream: they
+// issue the k-tiles (global -> LDS with global_load_lds_dwordx4, 16 bytes per lane),
+// wait for them and meet the compute waves at one barrier per k-tile. The first 4
+// (or 8, for 256x192 tiles: two per SIMD) only compute: MFMA from LDS, then the
+// epilogue's stores, which drain in the background while the loaders keep up to
+// STAGES-1 k-tiles of the next item in flight. The ring holds 2-8 stages (about
+// 112-144 KB of LDS).
 //
 // LDS rows are 128 bytes (64 halfs of k) or 64 bytes (64 E4M3 codes) with their
 // 16-byte chunks XOR-swizzled by row, so the MFMA fragment reads are free of bank
@@ -42,12 +43,12 @@ namespace onetrans {
 namespace {
 
 // SIDE (0 = shared S weights, 1 = private NS weights) only names the instance.
-// Waves 0-3 compute (a WM x (4/WM) grid over the tile), waves 4-7 load.
-template <int KIND, bool FP8, int SIDE, int BM, int BN, int STAGES, int WM>
-__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_m, int n_tiles_n, int n_items,
-                                                      int n_fast) {
+// Waves 0 .. CW-1 compute (a WM x (CW/WM) grid over the tile), the next four load.
+template <int KIND, bool FP8, int SIDE, int BM, int BN, int STAGES, int WM, int CW>
+__global__ __launch_bounds__((CW + 4) * 64, 1) void gemm_kernel(GemmParams p, int n_tiles_m, int n_tiles_n,
+                                                               int n_items, int n_fast) {
   constexpr int BK = 64;
-  constexpr int WN = 4 / WM;
+  constexpr int WN = CW / WM;
   constexpr int TM = BM / WM, TN = BN / WN;  // one compute wave's part of the tile
   constexpr int MI = TM / 32, NI = TN / 32;  // 32x32 blocks per compute wave
   constexpr int AROW = BK * 2;               // bytes per LDS row: fp16 activations
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
   constexpr int PT = A_INSTR + B_INSTR;
   constexpr int A_RPI = 1024 / AROW, B_RPI = 1024 / BROW;  // rows per DMA instruction
   constexpr int A_CPR = AROW / 16, B_CPR = BROW / 16;      // 16-byte chunks per row
-  static_assert(WM * WN == 4 && TM % 32 == 0 && TN % 32 == 0, "wave grid");
+  static_assert((CW == 4 || CW == 8) && WM * WN == CW && TM % 32 == 0 && TN % 32 == 0, "wave grid");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "tile shape");
   static_assert(STAGES >= 2 && STAGES * STAGE <= 159 * 1024, "LDS");
   static_assert(PT * (STAGES - 2) < 64, "vmcnt range");
@@ -88,9 +89,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
     else { mt = r % n_tiles_m; nt = r / n_tiles_m; }
   };
 
-  if (wave >= 4) {
+  if (wave >= CW) {
     // ================= loader waves: the only waves that touch vmcnt for operands =================
-    const int lw = wave - 4;
+    const int lw = wave - CW;
     const char* a_src[A_INSTR];
     const char* b_src[B_INSTR];
     int iss_t = 0, iss_kt = 0;  // item and k-tile of the next step to issue
@@ -141,12 +142,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
   const int wm = wave / WN, wn = wave % WN;
   constexpr int KS = BK / 16;  // 16-wide k-steps per k-tile (even: the fragment buffers alternate)
   static_assert(KS % 2 == 0, "k-steps per tile");
-  // Fragments of one k-step, double-buffered: the reads of step ks + 1 are issued before the
-  // MFMAs of step ks, so LDS latency hides under them. E4M3 weights stay as codes until the
-  // MFMA that takes them.
-  f16x8 af[2][MI];
-  f16x8 bf[2][FP8 ? 1 : NI];
-  uint2 b8[2][FP8 ? NI : 1];
+  // Fragments of one k-step, double-buffered with four compute waves: the reads of step
+  // ks + 1 are issued before the MFMAs of step ks, so LDS latency hides under them. With
+  // eight (two per SIMD) the other wave's MFMAs cover it and one buffer keeps registers
+  // for the accumulators. E4M3 weights stay as codes until the MFMA that takes them.
+  constexpr int NBUF = CW == 8 ? 1 : 2;
+  f16x8 af[NBUF][MI];
+  f16x8 bf[NBUF][FP8 ? 1 : NI];
+  uint2 b8[NBUF][FP8 ? NI : 1];
   auto read_frags = [&](int s, int ks, int b) {
     const char* st = smem + (s % STAGES) * STAGE;
     const int c = 2 * ks + (lane >> 5);
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
   // the first step's tile is in LDS (one barrier per step, as the loaders)
   if (my_items > 0) {
     lds_barrier();
-    read_frags(0, 0, 0);
+    if constexpr (NBUF == 2) read_frags(0, 0, 0);
   }
 #pragma unroll 1
   for (int t = 0; t < my_items; ++t) {
@@ -187,6 +190,24 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
       const int s = t * nk + kt;
+      if constexpr (NBUF == 1) {
+        if (s > 0) lds_barrier();  // certifies step s and hands step s - 1's stage back
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          read_frags(s, ks, 0);
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            f16x8 wf;
+            if constexpr (FP8) wf = e4m3x8_to_f16(b8[0][ni]);
+            else wf = bf[0][ni];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, af[0][mi], acc[mi][ni], 0, 0, 0);
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int b = ks & 1;
@@ -194,22 +215,22 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p, int n_tiles_
         // reads are issued keeps the compiler from waiting for those as well
         __builtin_amdgcn_s_waitcnt(0xC07F);
         if (ks + 1 < KS) {
-          read_frags(s, ks + 1, b ^ 1);
+          read_frags(s, ks + 1, (b ^ 1) % NBUF);
         } else if (s + 1 < total_steps) {
           // every wave has read its last fragments of step s: the barrier hands that stage
           // back to the loaders and certifies step s + 1, whose first fragments are read now
           lds_barrier();
-          read_frags(s + 1, 0, b ^ 1);
+          read_frags(s + 1, 0, (b ^ 1) % NBUF);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           f16x8 wf;
-          if constexpr (FP8) wf = e4m3x8_to_f16(b8[b][ni]);
-          else wf = bf[b][ni];
+          if constexpr (FP8) wf = e4m3x8_to_f16(b8[b % NBUF][ni]);
+          else wf = bf[b % NBUF][ni];
 #pragma unroll
           for (int mi = 0; mi < MI; ++mi)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, af[b][mi], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, af[b % NBUF][mi], acc[mi][ni], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -333,25 +354,25 @@ constexpr int stages_for() {
   return n > 8 ? 8 : n;
 }
 
-template <int KD, bool FP8, int SIDE, int BM, int BN, int WM>
+template <int KD, bool FP8, int SIDE, int BM, int BN, int WM, int CW>
 void launch_one(const GemmParams& p, hipStream_t s) {
   const int tm = (p.M + BM - 1) / BM, tn = p.N / BN;
   const long items = (long)tm * tn * p.groups;
   const int grid = (int)(items < 256 ? items : 256);  // one workgroup per CU
   const int n_fast = (long)p.M > (long)p.N ? 1 : 0;  // a group's rows: activations M x K, weights N x K
-  hipLaunchKernelGGL((gemm_kernel<KD, FP8, SIDE, BM, BN, stages_for<KD, BM, BN, WM, FP8>(), WM>), dim3(grid), dim3(512), 0, s,
-                     p, tm, tn, (int)items, n_fast);
+  hipLaunchKernelGGL((gemm_kernel<KD, FP8, SIDE, BM, BN, stages_for<KD, BM, BN, WM, FP8>(), WM, CW>), dim3(grid),
+                     dim3((CW + 4) * 64), 0, s, p, tm, tn, (int)items, n_fast);
 }
 
-template <int KD, int SIDE, int BM, int BN, int WM>
+template <int KD, int SIDE, int BM, int BN, int WM, int CW = 4>
 void launch_cfg(bool fp8, const GemmParams& p, hipStream_t s) {
   if constexpr (SIDE == 1 && BN != 96) {
     if (fp8) {
-      launch_one<KD, true, SIDE, BM, BN, WM>(p, s);
+      launch_one<KD, true, SIDE, BM, BN, WM, CW>(p, s);
       return;
     }
   }
-  launch_one<KD, false, SIDE, BM, BN, WM>(p, s);
+  launch_one<KD, false, SIDE, BM, BN, WM, CW>(p, s);
 }
 
 struct TileCfg {
@@ -368,25 +389,31 @@ double tile_cost(const GemmParams& p, bool fp8, int bm, int bn) {
 template <int KD, int SIDE>
 void launch_kind(bool fp8, const GemmParams& p, hipStream_t s) {
   // a Q / K / V tile must not straddle two of them: BN divides d
-  auto fits = [&](int bn) { return p.N % bn == 0 && (KD != GEMM_QKV || p.d % bn == 0) && !(fp8 && bn == 96); };
+  auto fits = [&](int bn) {
+    return p.N % bn == 0 && (KD != GEMM_QKV || p.d % bn == 0) && !(fp8 && bn == 96) &&
+           !(KD == GEMM_FFN_DOWN && bn == 192);
+  };
   // ties go to the earlier entry: the smaller tile, which leaves fewer CUs idle in the last round
-  const TileCfg cands[6] = {{128, 96}, {128, 128}, {256, 96}, {256, 128}, {128, 64}, {64, 64}};
+  const TileCfg cands[7] = {{128, 96}, {128, 128}, {256, 96}, {256, 128}, {128, 64}, {64, 64}, {256, 192}};
   int best = -1;
   double best_cost = 0;
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < 7; ++i) {
     if (!fits(cands[i].bn)) continue;
     const double c = tile_cost(p, fp8, cands[i].bm, cands[i].bn);
     if (best < 0 || c < best_cost) { best = i; best_cost = c; }
   }
-  // one 256x192 tile per workgroup (fp16 weights, every tile on the chip at once) when the
-  // same cost model prefers it
-  if constexpr (KD != GEMM_FFN_DOWN) {
-    if (!fp8 && p.M <= 256 && fits(192) && (long)(p.N / 192) * p.groups <= 256 &&
-        tile_cost(p, false, 256, 192) < best_cost) {
-      const int tn = p.N / 192;
-      hipLaunchKernelGGL((gemm_tile256_kernel<KD, SIDE>), dim3(tn * p.groups), dim3(512), 0, s, p, tn);
-      return;
+  // 256x192: one tile per workgroup (fp16 weights, every tile on the chip at once), else
+  // persistent with eight compute waves
+  if (best == 6) {
+    if constexpr (KD != GEMM_FFN_DOWN) {  // (never picked for FFN down: see fits)
+      if (!fp8 && p.M <= 256 && (long)(p.N / 192) * p.groups <= 256) {
+        const int tn = p.N / 192;
+        hipLaunchKernelGGL((gemm_tile256_kernel<KD, SIDE>), dim3(tn * p.groups), dim3(512), 0, s, p, tn);
+        return;
+      }
+      launch_cfg<KD, SIDE, 256, 192, 4, 8>(fp8, p, s);
     }
+    return;
   }
   switch (best) {
     case 0: launch_cfg<KD, SIDE, 128, 96, 4>(fp8, p, s); break;
