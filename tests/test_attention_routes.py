@@ -43,6 +43,11 @@ def test_dispatch_thresholds(lib):
     assert route(lib, False, 64, 32 * 1023, 2, 1) == "attn_kernel<64,2>"
     assert route(lib, False, 64, 32 * 1024, 2, 1) == "attn_kernel<64,4>"
     assert route(lib, False, 32, 32 * 100, 2, 3) == "attn_split_kernel<32,4,true>"
+    # several users with 2-4 query blocks each (appends): the tile kernel, two blocks a workgroup
+    assert route(lib, False, 64, 64, 6, 64) == "attn_kernel<64,2>"
+    assert route(lib, False, 64, 128, 6, 8) == "attn_kernel<64,2>"
+    assert route(lib, False, 64, 129, 6, 8) == "attn_split_kernel<64,5,true>"
+    assert route(lib, False, 32, 32, 6, 64) == "attn_split_kernel<32,4,true>"
     assert route(lib, True, 64, 32 * 511, 2, 1) == "attn_ns2_kernel<64,1>"
     assert route(lib, True, 32, 32 * 512, 2, 1) == "attn_ns2_kernel<32,2>"
     assert route(lib, False, 48, 32, 2, 1) == "none"

@@ -181,9 +181,8 @@ def test_persistent_eight_wave_gemms(wdtype):
     assert_close(got.cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, ns[0]), wdtype, "NS rows")
 
 
-# appends to many users with several query blocks per (user, head) in the S attention (the
-# split kernel with the blocks of a (user, head) grouped on one XCD); 80 new events leave
-# a ragged block
+# appends to many users with several query blocks per (user, head) in the S attention (two
+# blocks per workgroup of the tile kernel); 80 new events leave a ragged block
 MANY_APPENDS = {
     "k_dh32_64users_m80": (Workload(name="k", n_layers=2, d_model=64, n_heads=2, ffn_hidden=128, s_len=300,
                                     q_sched=(300, 150), n_ns=4, n_users=64, n_candidates=2), 80),
@@ -197,7 +196,7 @@ def test_many_user_append_several_query_blocks(name):
     from unified_transformer_recommender_onetrans_amd._capi import lib
     wl, m = MANY_APPENDS[name]
     B = wl.n_users
-    assert lib().onetrans_attention_route(0, wl.head_dim, m, wl.n_heads, B).decode().endswith(",true>")
+    assert lib().onetrans_attention_route(0, wl.head_dim, m, wl.n_heads, B).decode() == f"attn_kernel<{wl.head_dim},2>"
     print(f"case {name}: B={B} m={m}", flush=True)
     mdl, lay = model(wl, append_cap=m)
     base = [300, 0, 1, 33, 64, 65, 127, 128, 129, 200, 255, 256, 257, 299]

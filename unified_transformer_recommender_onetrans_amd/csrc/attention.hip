@@ -941,9 +941,11 @@ void launch_attn_nw(const AttnParams& p, int n_seg, hipStream_t s) {
 // waves) per workgroup when there are blocks for 512 such workgroups, else 1. S: with few
 // query blocks (one user's prefill, appends) each block's keys are split over five waves
 // (head dim 64: their double-buffered tile rings fill the 160 KB of LDS; four for head dim
-// 32), the blocks of one (user, head) grouped on one XCD when there are several users; with many
-// (a batch of users' prefill) 4 or 2 query blocks share a workgroup's key stream. The K/V of
-// a layer is L2-resident, so streaming it to more workgroups is cheap.
+// 32), the blocks of one (user, head) grouped on one XCD when there are several users, except
+// for several users with 2-4 blocks each (appends), whose key-split workgroups would hold a
+// CU each with five waves: there two blocks share a tile-kernel workgroup (three per CU).
+// With many (a batch of users' prefill) 4 or 2 query blocks share a workgroup's key stream.
+// The K/V of a layer is L2-resident, so streaming it to more workgroups is cheap.
 AttnRoute attention_route(bool ns, int dh, int nq, int H, int n_seg) {
   const long blocks32 = (long)((nq + 31) / 32) * H * n_seg;
   const bool d64 = dh == 64;
@@ -952,6 +954,9 @@ AttnRoute attention_route(bool ns, int dh, int nq, int H, int n_seg) {
     return d64 ? ATTN_NS2_64_1 : ATTN_NS2_32_1;
   }
   if (blocks32 < 2L * 512) {
+    // several users with 2-4 query blocks each (appends): two blocks share a workgroup's
+    // key stream, three such workgroups per CU
+    if (n_seg > 1 && nq > 32 && nq <= 128) return d64 ? ATTN_TILE_64_2 : ATTN_TILE_32_2;
     if (n_seg > 1) return d64 ? ATTN_SPLIT_64_GROUPED : ATTN_SPLIT_32_GROUPED;
     return d64 ? ATTN_SPLIT_64 : ATTN_SPLIT_32;
   }
