@@ -57,25 +57,19 @@ struct Softmax {
   f32x16 o[DH / 32];
 };
 
-// Online-softmax update with NB 32-key blocks of raw scores (masked entries -inf). With
-// SUM false the caller adds the probabilities' sum to l itself (attn_tile does it on the
-// matrix core).
-// The scale 1/sqrt(dh) * log2(e) is applied inside exp2 as one fma. The O
-// accumulators are rescaled only when some lane's reference max moved: otherwise
-// the factor is exactly 1 and the multiply is skipped. Without LAZY the reference is the
-// running max; with LAZY it moves only when a block's max exceeds it by more than 8 in
-// log2 units (probabilities then stay below 2^8; any reference gives the same normalised
-// result), so after the first keys of a query the rescale is almost never taken, where
-// the running max of some lane of a wave grows at nearly every tile of a long key range.
-// Returns the bf16 probabilities packed as the B operands of the P.V product.
-template <int DH, int NB, bool SUM = true, bool LAZY = false>
+// Online-softmax update with NB 32-key blocks of raw scores (masked entries -inf), the
+// running max as reference. The scale 1/sqrt(dh) * log2(e) is applied inside exp2 as one
+// fma. The O accumulators are rescaled only when some lane's max moved: otherwise the
+// factor is exactly 1 and the multiply is skipped. Returns the bf16 probabilities packed
+// as the B operands of the P.V product.
+template <int DH, int NB>
 __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&sc)[NB], bf16x8 (&pb)[NB][2],
                                                float scale) {
   float mt = vmax16(sc[0]);
 #pragma unroll
   for (int b = 1; b < NB; ++b) mt = vmax(mt, vmax16(sc[b]));
   mt = max_halves(mt);
-  const float m_new = LAZY ? (mt > st.m + 8.f / scale ? mt : st.m) : fmaxf(st.m, mt);
+  const float m_new = fmaxf(st.m, mt);
   if (__builtin_amdgcn_ballot_w64(m_new > st.m) != 0) {
     const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((st.m - m_new) * scale);
     st.l *= alpha;
@@ -94,10 +88,10 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&s
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(sc[b][8 * c + i], scale, msub));
-        if (SUM) ps += pv;
+        ps += pv;
         pb[b][c][i] = (__bf16)pv;
       }
-  if (SUM) st.l += ps;
+  st.l += ps;
 }
 
 // Pieces of one 64-key tile against a wave's 32 queries. sb holds the tile: K rows
@@ -144,48 +138,61 @@ __device__ __forceinline__ void mask_tile(f32x16 (&sc)[2], int t0, int key_lo, i
     }
 }
 
-// O^T += V^T P^T with the tile's bf16 probabilities
+// One whole tile: scores, masking when a bound falls inside it, then the two 32-key halves
+// in turn: the half's max against the lazy reference (moved, with a rescale of l and O,
+// only when it passes the reference by more than 8 in log2 units), its exponentials and
+// its P.V. Going half by half lets the second half's score MFMAs run under the first
+// half's softmax and the first half's P.V under the second half's exponentials; a wave
+// that has its SIMD to itself (the key-split kernel) otherwise waits for each in turn.
 template <int DH>
-__device__ __forceinline__ void pv_tile(const char* sb, const bf16x8 (&pb)[2][2], Softmax<DH>& st) {
+__device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, int my_lim, bool edge,
+                                          const bf16x8 (&qf)[DH / 16], Softmax<DH>& st, float scale) {
   constexpr int KROW = DH * 2, K_BYTES = KT * KROW;
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  f32x16 sc[2];
+  qk_tile<DH>(sb, qf, sc);
+  if (edge) mask_tile(sc, t0, key_lo, my_lim);
+  const float tau = 8.f / scale;
+  bf16x8 ones;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const float mt = max_halves(vmax16(sc[kb]));
+    if (__builtin_amdgcn_ballot_w64(mt > st.m + tau) != 0) {
+      const bool up = mt > st.m + tau;
+      const float alpha = up ? __builtin_amdgcn_exp2f((st.m - mt) * scale) : 1.f;
+      if (up) st.m = mt;
+      st.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st.o[db][j] *= alpha;
+    }
+    const float msub = st.m == -INFINITY ? 0.f : -st.m * scale;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kb][8 * c + i], scale, msub));
+    // O^T += V^T P^T over this half's keys kb*32 + 16c + 8*half + 0..7
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db) {
-        // keys kb*32 + 16c + 8*half + 0..7: 16-byte chunk 4kb + 2c + half of V^T row r
         const int r = db * 32 + l32;
         const int ch = 4 * kb + 2 * c + half;
         const bf16x8 a = *(const bf16x8*)(sb + K_BYTES + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][c], st.o[db], 0, 0, 0);
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], st.o[db], 0, 0, 0);
       }
-}
-
-// One whole tile: scores, masking when a bound falls inside it, the online-softmax update
-// and the P.V product.
-template <int DH>
-__device__ __forceinline__ void attn_tile(const char* sb, int t0, int key_lo, int my_lim, bool edge,
-                                          const bf16x8 (&qf)[DH / 16], Softmax<DH>& st, float scale) {
-  f32x16 sc[2];
-  qk_tile<DH>(sb, qf, sc);
-  if (edge) mask_tile(sc, t0, key_lo, my_lim);
-  bf16x8 pb[2][2];
-  softmax_update<DH, 2, false, true>(st, sc, pb, scale);
-  pv_tile<DH>(sb, pb, st);
-  // the tile's probability sum on the matrix core: an all-ones A operand turns every
-  // output row of 1 P^T into the column sums (the same bf16 P that multiplies V). Both
-  // half-waves get the full sum (bit-identical rows) while l is kept as per-half partial
-  // sums that are added at the end, so each half adds half of it (exact in fp32).
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
-  f32x16 ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0][0], f32x16{}, 0, 0, 0);
-  ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0][1], ls, 0, 0, 0);
-  ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[1][0], ls, 0, 0, 0);
-  ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[1][1], ls, 0, 0, 0);
-  st.l += 0.5f * ls[0];
+    // the half's probability sum on the matrix core: an all-ones A operand turns every
+    // output row of 1 P^T into the column sums (the same bf16 P that multiplies V). Both
+    // half-waves get the full sum while l is kept as per-half partial sums that are added
+    // at the end, so each half adds half of it (exact in fp32).
+    f32x16 ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0], f32x16{}, 0, 0, 0);
+    ls = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[1], ls, 0, 0, 0);
+    st.l += 0.5f * ls[0];
+  }
 }
 
 // Output of query row qi, in two parts. out_row_load fetches this lane's half of head h's
