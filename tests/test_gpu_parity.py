@@ -164,10 +164,11 @@ def test_one_tile_per_workgroup_gemms():
 
 
 @pytest.mark.parametrize("wdtype", ["bf16", "e4m3"])
-def test_persistent_eight_wave_gemms(wdtype):
+def test_256x192_gemms_with_more_tiles_than_cus(wdtype):
     """2048 candidates x 16 NS positions at d = 192, F = 384: the NS QKV (N = 576) and FFN up
-    (N = 384) GEMMs take 256x192 tiles on the persistent kernel with eight compute waves
-    (several tiles per workgroup, M > 256); every output is compared."""
+    (N = 384) GEMMs take 256x192 tiles, 384 and 256 of them over 8 row tiles (bf16: one tile
+    per workgroup; E4M3: the persistent kernel with eight compute waves, several tiles per
+    workgroup); every output is compared."""
     wl = Workload(name="p8", n_layers=2, d_model=192, n_heads=3, ffn_hidden=384, s_len=160,
                   q_sched=(160, 40), n_ns=16, n_users=1, n_candidates=2048, ns_wdtype=wdtype)
     m, lay = model(wl)

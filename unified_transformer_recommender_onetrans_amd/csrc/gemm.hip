@@ -23,7 +23,7 @@
 // stores whenever it waits for a k-tile. Here the last four waves only stream: they
 // issue the k-tiles (global -> LDS with global_load_lds_dwordx4, 16 bytes per lane),
 // wait for them and meet the compute waves at one barrier per k-tile. The first 4
-// (or 8, for 256x192 tiles: two per SIMD) only compute: MFMA from LDS, then the
+// (or 8, for 256x192 tiles of E4M3 weights: two per SIMD) only compute: MFMA from LDS, then the
 // epilogue's stores, which drain in the background while the loaders keep up to
 // STAGES-1 k-tiles of the next item in flight. The ring holds 2-8 stages (about
 // 112-144 KB of LDS).
@@ -240,17 +240,19 @@ __global__ __launch_bounds__((CW + 4) * 64, 1) void gemm_kernel(GemmParams p, in
   }
 }
 
-// One 256x192 output tile per workgroup (no persistence), for launches whose tiles all fit
-// on the chip at once: fewer operand bytes per CU than two or three smaller tiles (each
-// weight row is fetched once per 256 rows, each activation row once per 192 columns).
-// With one tile per workgroup no epilogue store ever precedes a k-tile wait, so all 8
+// One 256x192 output tile per workgroup (no persistence; with more tiles than CUs the
+// hardware starts each workgroup as a CU frees up), for fp16 weights: fewer operand bytes
+// per CU than smaller tiles (each weight row is fetched once per 256 rows, each activation
+// row once per 192 columns), and a workgroup that starts late (its CU held by concurrent
+// work) delays one tile only. With one tile per workgroup no epilogue store ever precedes
+// a k-tile wait, so all 8
 // waves both stream operands and compute (a 4 x 2 grid of 64x96 parts, 96 accumulators
 // per lane at two waves per SIMD). k-tiles are 64 wide, so every row of a k-tile is one
 // whole 128-byte line (a weight k-tile is six contiguous 4 KB panel blocks); the 56 KB
 // stages leave room for a ring of two (the next k-tile streams while this one is
 // multiplied). Each k-tile is 56 DMA instructions of 1 KB, 4 of A and 3 of B per wave.
 template <int KIND, int SIDE>
-__global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int n_tiles_n) {
+__global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
   constexpr int BM = 256, BN = 192, BK = 64, STAGES = 2;
   constexpr int WN = 2, TM = 64, TN = 96, MI = TM / 32, NI = TN / 32;
   constexpr int ROW = BK * 2;  // bytes per LDS row (fp16)
@@ -266,10 +268,11 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
   const int nk = K / BK;
   // tile of this workgroup: each XCD (workgroup L runs on XCD L % 8) takes a contiguous range
   // of tiles, the N index fastest, so the tiles of one activation block share that XCD's L2
+  // (then M, then the group)
   const int total = gridDim.x, L = blockIdx.x;
   const int x = L % N_XCD, w = x * (total / N_XCD) + min(x, total % N_XCD) + L / N_XCD;
-  const int nt = w % n_tiles_n, g = w / n_tiles_n;  // one M tile per group (M <= 256)
-  const int n0 = nt * BN;
+  const int nt = w % n_tiles_n, mt = (w / n_tiles_n) % n_tiles_m, g = w / (n_tiles_n * n_tiles_m);
+  const int n0 = nt * BN, m0 = mt * BM;
 
   // per-lane DMA sources: A instructions 4w .. 4w+3, B instructions 3w .. 3w+2
   const char* a_src[4];
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (4 * wave + i) * RPI + lane / CPR;
-    const int row = min(r, M - 1);
+    const int row = min(m0 + r, M - 1);
     int seg, tt;
     split_row(row, rm.rows_per_seg, inv_rps, seg, tt);
     a_src[i] = (const char*)(p.a_in + hid_row(rm, seg, tt, g) * (long)K) + (swz<ROW>(lane % CPR, r) << 4);
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
   TilePre<KIND, MI, NI> pre;
-  tile_prefetch<KIND, MI, NI, TM, TN>(p, 0, n0, g, wm, wn, pre);
+  tile_prefetch<KIND, MI, NI, TM, TN>(p, m0, n0, g, wm, wn, pre);
 
   for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
 #pragma unroll 1
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(GemmParams p, int 
         for (int mi = 0; mi < MI; ++mi)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[ks][ni], af[ks][mi], acc[mi][ni], 0, 0, 0);
   }
-  tile_epilogue<KIND, false, MI, NI, TM, TN>(p, acc, 0, n0, g, wm, wn, pre);
+  tile_epilogue<KIND, false, MI, NI, TM, TN>(p, acc, m0, n0, g, wm, wn, pre);
 }
 
 // Tile shapes: (BM, BN, compute waves along M). 96-wide tiles are fp16-only (a 96-row E4M3
@@ -402,16 +405,16 @@ void launch_kind(bool fp8, const GemmParams& p, hipStream_t s) {
     const double c = tile_cost(p, fp8, cands[i].bm, cands[i].bn);
     if (best < 0 || c < best_cost) { best = i; best_cost = c; }
   }
-  // 256x192: one tile per workgroup (fp16 weights, every tile on the chip at once), else
-  // persistent with eight compute waves
+  // 256x192: one tile per workgroup with fp16 weights, persistent with eight compute waves
+  // with E4M3 weights
   if (best == 6) {
     if constexpr (KD != GEMM_FFN_DOWN) {  // (never picked for FFN down: see fits)
-      if (!fp8 && p.M <= 256 && (long)(p.N / 192) * p.groups <= 256) {
-        const int tn = p.N / 192;
-        hipLaunchKernelGGL((gemm_tile256_kernel<KD, SIDE>), dim3(tn * p.groups), dim3(512), 0, s, p, tn);
+      if (!fp8) {
+        const int tn = p.N / 192, tm = (p.M + 255) / 256;
+        hipLaunchKernelGGL((gemm_tile256_kernel<KD, SIDE>), dim3(tm * tn * p.groups), dim3(512), 0, s, p, tn, tm);
         return;
       }
-      launch_cfg<KD, SIDE, 256, 192, 4, 8>(fp8, p, s);
+      if constexpr (SIDE == 1) launch_one<KD, true, SIDE, 256, 192, 4, 8>(p, s);  // E4M3: NS weights only
     }
     return;
   }
