@@ -49,6 +49,10 @@ MANY_USERS = {
                                q_sched=(2048, 1024), n_ns=4, n_users=16, n_candidates=3),
     "j_dh64_12users": Workload(name="j", n_layers=2, d_model=128, n_heads=2, ffn_hidden=256, s_len=2048,
                                q_sched=(2048, 1000), n_ns=4, n_users=12, n_candidates=3),
+    # d = 192, F = 768: the S QKV and FFN up GEMMs of 24k and 12k rows take 256x192 tiles,
+    # one per workgroup, many per group
+    "m_d192_12users": Workload(name="m", n_layers=2, d_model=192, n_heads=3, ffn_hidden=768, s_len=2048,
+                               q_sched=(2048, 1000), n_ns=4, n_users=12, n_candidates=3),
 }
 
 
