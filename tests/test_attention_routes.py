@@ -1,6 +1,6 @@
 """Which attention kernel instance each launch takes (host dispatch logic, no GPU).
 
-The library compiles twelve attention instances; the dispatch picks one from the
+The library compiles sixteen attention instances; the dispatch picks one from the
 query count per (segment, head), the head count and the number of segments. These
 tests pin that the GPU parity workloads together reach every compiled instance, so
 no instance is left unexercised by the element-wise comparisons against the oracle.
@@ -13,6 +13,8 @@ from unified_transformer_recommender_onetrans_amd import _capi as C
 
 ALL_ROUTES = {
     "attn_ns2_kernel<64,2>", "attn_ns2_kernel<64,1>", "attn_ns2_kernel<32,2>", "attn_ns2_kernel<32,1>",
+    "attn_split_kernel<64,5,true,ns>", "attn_split_kernel<32,4,true,ns>", "attn_split_kernel<64,5,false,ns>",
+    "attn_split_kernel<32,4,false,ns>",
     "attn_split_kernel<64,5,true>", "attn_split_kernel<32,4,true>", "attn_split_kernel<64,5,false>",
     "attn_split_kernel<32,4,false>", "attn_kernel<64,4>", "attn_kernel<32,4>", "attn_kernel<64,2>",
     "attn_kernel<32,2>",
@@ -49,6 +51,11 @@ def test_dispatch_thresholds(lib):
     assert route(lib, False, 64, 129, 6, 8) == "attn_split_kernel<64,5,true>"
     assert route(lib, False, 32, 32, 6, 64) == "attn_split_kernel<32,4,true>"
     assert route(lib, True, 64, 32 * 511, 2, 1) == "attn_ns2_kernel<64,1>"
+    # NS with at most 256 query blocks: keys split over five (four) waves per block
+    assert route(lib, True, 64, 32 * 128, 2, 1) == "attn_split_kernel<64,5,false,ns>"
+    assert route(lib, True, 64, 32 * 129, 2, 1) == "attn_ns2_kernel<64,1>"
+    assert route(lib, True, 64, 8, 6, 42) == "attn_split_kernel<64,5,true,ns>"
+    assert route(lib, True, 32, 5, 2, 3) == "attn_split_kernel<32,4,true,ns>"
     assert route(lib, True, 32, 32 * 512, 2, 1) == "attn_ns2_kernel<32,2>"
     assert route(lib, False, 48, 32, 2, 1) == "none"
     assert route(lib, False, 64, 0, 2, 1) == "none"
@@ -66,6 +73,10 @@ def test_gpu_parity_workloads_reach_every_instance(lib):
         reached.add(route(lib, True, wl.head_dim, wl.n_candidates * wl.n_ns, wl.n_heads, 1))
         for m in (13, 6):
             reached.add(route(lib, False, wl.head_dim, m, wl.n_heads, B))
+    # user-side NS passes (one segment per user) and their candidates
+    for wl, lens, Pu in G.USER_NS.values():
+        reached.add(route(lib, True, wl.head_dim, Pu, wl.n_heads, len(lens)))
+        reached.add(route(lib, True, wl.head_dim, wl.n_candidates * (wl.n_ns - Pu), wl.n_heads, 1))
     # many-user prefills (test_many_user_prefill_tile_kernels)
     for wl in G.MANY_USERS.values():
         reached.update(prefill_routes(lib, wl, wl.n_users))

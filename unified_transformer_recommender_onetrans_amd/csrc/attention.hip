@@ -771,12 +771,15 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   out_row_store<DH, false>(p, seg, h, qi, orow, st.o, inv);
 }
 
-// S-token attention with the keys of one 32-query block split over KS waves: wave w takes
-// key tiles w, w + KS, ... through a private 2-stage LDS ring (no barriers while
-// streaming), and the partial (max, sum, O) of the waves merge through LDS at the end.
-// Used when there are few query blocks and long key ranges (one user's prefill, appends),
-// where the plain kernel's critical path is one wave walking every key tile.
-template <int DH, int KS, bool GROUPED>
+// Attention with the keys of one 32-query block split over KS waves: wave w takes key
+// tiles w, w + KS, ... through a private 2-stage LDS ring (no barriers while streaming),
+// and the partial (max, sum, O) of the waves merge through LDS at the end. Used when there
+// are few query blocks and long key ranges, where a plain kernel's critical path is one
+// wave walking every key tile: S queries of one user's prefill or of appends (causal
+// limits), and with NS the few NS queries of the user-side pass (every cached key
+// [key_lo, n_keys) visible; after the merge, wave 0 adds the user's cached NS rows and
+// the block's own NS keys as attn_ns2_kernel does).
+template <int DH, int KS, bool GROUPED, bool NS>
 __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   constexpr int KROW = DH * 2;
   constexpr int K_BYTES = KT * KROW;
@@ -829,9 +832,11 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   const int vf = p.valid_from[seg];
   const int key_lo = max(0, vf - p.key_pos0);
   const int qlast = min(wq0 + 31, p.nq - 1);
-  const int key_hi = min(p.n_keys, p.q_pos0 + qlast - p.key_pos0 + 1);  // exclusive, this block
-  const int lim_lo = wq0 + 31 < p.nq ? min(p.n_keys, p.q_pos0 + wq0 - p.key_pos0 + 1) : 0;
-  const int my_lim = q_ok ? min(p.n_keys, p.q_pos0 + qi - p.key_pos0 + 1) : 0;
+  // exclusive end of this block's keys, the end below which a tile needs no mask, this
+  // lane's end: causal for S queries, every cached key for NS queries
+  const int key_hi = NS ? p.n_keys : min(p.n_keys, p.q_pos0 + qlast - p.key_pos0 + 1);
+  const int lim_lo = wq0 + 31 < p.nq ? (NS ? p.n_keys : min(p.n_keys, p.q_pos0 + wq0 - p.key_pos0 + 1)) : 0;
+  const int my_lim = q_ok ? (NS ? p.n_keys : min(p.n_keys, p.q_pos0 + qi - p.key_pos0 + 1)) : 0;
 
   Softmax<DH> st;
 #pragma unroll
@@ -889,7 +894,7 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) mw[128 + (db * 16 + j) * 64 + lane] = st.o[db][j];
   __syncthreads();
-  if (wave != 0 || !q_ok) return;
+  if (wave != 0) return;
   float m_all = -INFINITY;
 #pragma unroll
   for (int w = 0; w < KS; ++w) m_all = fmaxf(m_all, ((const float*)(smem + w * MERGE))[lane]);
@@ -910,6 +915,67 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) o[db][j] += src[128 + (db * 16 + j) * 64 + lane] * f;
   }
+  if constexpr (NS) {
+    // the merged state continues (l kept as per-half partial sums again: each half-wave
+    // holds half of the full sum, exact in fp32) through the user's cached NS rows and the
+    // block's own NS keys, 32 row-major keys [t0, t0 + 32) at a time (rows past n_rows - 1
+    // are read as that row and masked), visible to this lane when vis(key) holds
+    Softmax<DH> st2;
+    st2.m = m_all;
+    st2.l = 0.5f * l_all;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db) st2.o[db] = o[db];
+    auto key_block = [&](const __bf16* knb, const __bf16* vnb, int n_rows, int t0, auto vis) {
+      f32x16 sk[1];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sk[0][j] = 0.f;
+      const int krow = min(t0 + l32, n_rows - 1);
+#pragma unroll
+      for (int s = 0; s < DH / 16; ++s) {
+        const bf16x8 a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
+        sk[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sk[0], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = t0 + 8 * (j >> 2) + half * 4 + (j & 3);
+        if (!(q_ok && vis(key))) sk[0][j] = -INFINITY;
+      }
+      bf16x8 pk[1][2];
+      softmax_update<DH, 1>(st2, sk, pk, p.scale_log2);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < DH / 32; ++db) {
+          bf16x8 a;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), n_rows - 1);
+            a[i] = vnb[(long)key * DH + db * 32 + l32];
+          }
+          st2.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][c], st2.o[db], 0, 0, 0);
+        }
+    };
+    if (p.n_x > 0) {
+      const __bf16* xkb = p.xk + h * p.x_head_stride;
+      const __bf16* xvb = p.xv + h * p.x_head_stride;
+      const int n_x = p.n_x;
+#pragma unroll 1
+      for (int t0 = 0; t0 < n_x; t0 += 32) key_block(xkb, xvb, n_x, t0, [&](int key) { return key < n_x; });
+    }
+    // query g = c*P + k sees own keys g' in [c*P, g]; NS K and V are row-major [H][nq][dh]
+    const int P = p.P;
+    const int g_lo = (wq0 / P) * P;
+    const int g_hi = min(wq0 + 31, p.nq - 1);
+    const int my_first = (qi / P) * P;
+#pragma unroll 1
+    for (int t0 = g_lo; t0 <= g_hi; t0 += 32)
+      key_block(p.kn + seg * p.kn_seg_stride + h * p.kn_head_stride, p.vn + seg * p.kn_seg_stride + h * p.kn_head_stride,
+                p.nq, t0, [&](int key) { return key <= qi && key >= my_first; });
+    l_all = st2.l + __shfl_xor(st2.l, 32);
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db) o[db] = st2.o[db];
+  }
+  if (!q_ok) return;
   const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
   out_row_store<DH, true>(p, seg, h, qi, orow, o, inv);
 }
@@ -945,7 +1011,9 @@ void launch_attn_nw(const AttnParams& p, int n_seg, hipStream_t s) {
 
 // Which kernel instance runs a launch: 32 queries per wave, a workgroup's waves share the
 // K/V tiles. NS: each tile's keys split over two waves per query block, 2 query blocks (4
-// waves) per workgroup when there are blocks for 512 such workgroups, else 1. S: with few
+// waves) per workgroup when there are blocks for 512 such workgroups, else 1; with at most
+// 256 blocks (the user-side pass, a handful of candidates) the key tiles split over five
+// waves per block as for S queries, so that one block's walk is not the launch. S: with few
 // query blocks (one user's prefill, appends) each block's keys are split over five waves
 // (head dim 64: their double-buffered tile rings fill the 160 KB of LDS; four for head dim
 // 32), the blocks of one (user, head) grouped on one XCD when there are several users, except
@@ -957,6 +1025,11 @@ AttnRoute attention_route(bool ns, int dh, int nq, int H, int n_seg) {
   const long blocks32 = (long)((nq + 31) / 32) * H * n_seg;
   const bool d64 = dh == 64;
   if (ns) {
+    // few NS query blocks (the user-side pass, a handful of candidates): keys split over waves
+    if (blocks32 <= 256) {
+      if (n_seg > 1) return d64 ? ATTN_NSSPLIT_64_GROUPED : ATTN_NSSPLIT_32_GROUPED;
+      return d64 ? ATTN_NSSPLIT_64 : ATTN_NSSPLIT_32;
+    }
     if (blocks32 >= 2L * 512) return d64 ? ATTN_NS2_64_2 : ATTN_NS2_32_2;
     return d64 ? ATTN_NS2_64_1 : ATTN_NS2_32_1;
   }
@@ -977,6 +1050,10 @@ const char* attention_route_name(AttnRoute r) {
     case ATTN_NS2_64_1: return "attn_ns2_kernel<64,1>";
     case ATTN_NS2_32_2: return "attn_ns2_kernel<32,2>";
     case ATTN_NS2_32_1: return "attn_ns2_kernel<32,1>";
+    case ATTN_NSSPLIT_64_GROUPED: return "attn_split_kernel<64,5,true,ns>";
+    case ATTN_NSSPLIT_32_GROUPED: return "attn_split_kernel<32,4,true,ns>";
+    case ATTN_NSSPLIT_64: return "attn_split_kernel<64,5,false,ns>";
+    case ATTN_NSSPLIT_32: return "attn_split_kernel<32,4,false,ns>";
     case ATTN_SPLIT_64_GROUPED: return "attn_split_kernel<64,5,true>";
     case ATTN_SPLIT_32_GROUPED: return "attn_split_kernel<32,4,true>";
     case ATTN_SPLIT_64: return "attn_split_kernel<64,5,false>";
@@ -1000,14 +1077,30 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
     case ATTN_NS2_64_1: launch_attn_ns2<64, 1>(p, n_seg, s); break;
     case ATTN_NS2_32_2: launch_attn_ns2<32, 2>(p, n_seg, s); break;
     case ATTN_NS2_32_1: launch_attn_ns2<32, 1>(p, n_seg, s); break;
+    case ATTN_NSSPLIT_64_GROUPED:
+      hipLaunchKernelGGL((attn_split_kernel<64, 5, true, true>), grouped_grid, dim3(320), 0, s, p);
+      break;
+    case ATTN_NSSPLIT_32_GROUPED:
+      hipLaunchKernelGGL((attn_split_kernel<32, 4, true, true>), grouped_grid, dim3(256), 0, s, p);
+      break;
+    case ATTN_NSSPLIT_64:
+      hipLaunchKernelGGL((attn_split_kernel<64, 5, false, true>), split_grid, dim3(320), 0, s, p);
+      break;
+    case ATTN_NSSPLIT_32:
+      hipLaunchKernelGGL((attn_split_kernel<32, 4, false, true>), split_grid, dim3(256), 0, s, p);
+      break;
     case ATTN_SPLIT_64_GROUPED:
-      hipLaunchKernelGGL((attn_split_kernel<64, 5, true>), grouped_grid, dim3(320), 0, s, p);
+      hipLaunchKernelGGL((attn_split_kernel<64, 5, true, false>), grouped_grid, dim3(320), 0, s, p);
       break;
     case ATTN_SPLIT_32_GROUPED:
-      hipLaunchKernelGGL((attn_split_kernel<32, 4, true>), grouped_grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((attn_split_kernel<32, 4, true, false>), grouped_grid, dim3(256), 0, s, p);
       break;
-    case ATTN_SPLIT_64: hipLaunchKernelGGL((attn_split_kernel<64, 5, false>), split_grid, dim3(320), 0, s, p); break;
-    case ATTN_SPLIT_32: hipLaunchKernelGGL((attn_split_kernel<32, 4, false>), split_grid, dim3(256), 0, s, p); break;
+    case ATTN_SPLIT_64:
+      hipLaunchKernelGGL((attn_split_kernel<64, 5, false, false>), split_grid, dim3(320), 0, s, p);
+      break;
+    case ATTN_SPLIT_32:
+      hipLaunchKernelGGL((attn_split_kernel<32, 4, false, false>), split_grid, dim3(256), 0, s, p);
+      break;
     case ATTN_TILE_64_4: launch_attn_nw<64, 4>(p, n_seg, s); break;
     case ATTN_TILE_32_4: launch_attn_nw<32, 4>(p, n_seg, s); break;
     case ATTN_TILE_64_2: launch_attn_nw<64, 2>(p, n_seg, s); break;

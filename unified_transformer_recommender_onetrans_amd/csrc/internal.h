@@ -193,6 +193,7 @@ hipError_t launch_attention(bool ns, int dh, const AttnParams& p, int n_seg, hip
 // The kernel instance launch_attention picks for nq queries per (segment, head).
 enum AttnRoute {
   ATTN_NS2_64_2, ATTN_NS2_64_1, ATTN_NS2_32_2, ATTN_NS2_32_1,
+  ATTN_NSSPLIT_64_GROUPED, ATTN_NSSPLIT_32_GROUPED, ATTN_NSSPLIT_64, ATTN_NSSPLIT_32,
   ATTN_SPLIT_64_GROUPED, ATTN_SPLIT_32_GROUPED, ATTN_SPLIT_64, ATTN_SPLIT_32,
   ATTN_TILE_64_4, ATTN_TILE_32_4, ATTN_TILE_64_2, ATTN_TILE_32_2,
   ATTN_ROUTE_COUNT
