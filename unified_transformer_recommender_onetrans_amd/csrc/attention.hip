@@ -13,12 +13,14 @@
 // leaves registers. The cached V is stored transposed ([dh][key]) so the V^T
 // operand is a plain row read.
 //
-// Data movement: each wave owns 32 queries; a workgroup of 4 waves shares K and
-// V^T tiles of 64 keys that travel global -> LDS with buffer_load_dwordx4 ... lds
-// (base in a buffer resource, so no per-lane 64-bit address arithmetic), three tiles in
-// flight. Tile rows are XOR-swizzled in 16-byte chunks so the
-// fragment reads are bank-conflict free. The result is added to the fp32
-// residual rows (z = x + o) without rounding.
+// Data movement: each wave owns 32 queries; K and V^T tiles of 64 keys travel global ->
+// LDS with buffer_load_dwordx4 ... lds (base in a buffer resource, so no per-lane 64-bit
+// address arithmetic). Three kernels: the tile kernel (the waves of a workgroup share a
+// ring of three tiles), the NS kernel (two waves per query block, each scoring one 32-key
+// half of every tile of a shared ring) and the key-split kernel (waves of one query block
+// take every KS-th tile through private rings, merged at the end). Tile rows are
+// XOR-swizzled in 16-byte chunks so the fragment reads are bank-conflict free. The result
+// is added to the fp32 residual rows (z = x + o) without rounding.
 #include <math.h>
 
 #include <type_traits>
