@@ -37,8 +37,9 @@
  *   - Matrices use the torch Linear layout [out][in]; all arrays are dense,
  *     row-major and 16-byte aligned.
  *   - Numerics: RMSNorm, softmax and the residual stream in fp32; the five
- *     linear maps take fp16 operands (bf16 weights converted exactly at pack
- *     time, E4M3FN weights decoded exactly) with fp32 accumulation; attention
+ *     linear maps take fp16 operands (bf16 weights converted at pack time, exact
+ *     inside the range stated at onetrans_pack_weights; E4M3FN weights decoded
+ *     exactly) with fp32 accumulation; attention
  *     takes bf16 Q, K, V and probabilities with fp32 accumulation. A norm
  *     feeding a linear map is applied as r * ((x * g) W): the operand is
  *     x * g rounded to fp16 and the row factor r = 1/sqrt(mean(x^2) + eps)
