@@ -93,7 +93,9 @@ def test_kernel_work_sums_to_step_flops():
     total = sum(f for f, _ in w.values())
     want = bench.prefill_flops(wl, [1500]) + 256 * bench.score_flops_per_candidate(wl, nk)
     assert abs(total - want) / want < 1e-12
-    assert abs(bench.prefill_flops(wl, [1500]) / 1e9 - 27.0) < 0.01          # survey figure
+    # 27.0 GFLOP per full-length prefill and 1.208 GFLOP per candidate, counted by hand from
+    # the OneTrans-L shape (2 per MAC over the needed rows, 4 d per visible pair)
+    assert abs(bench.prefill_flops(wl, [1500]) / 1e9 - 27.0) < 0.01
     assert abs(bench.score_flops_per_candidate(wl, nk) / 1e9 - 1.208) < 1e-3
 
 
