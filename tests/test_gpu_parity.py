@@ -39,6 +39,12 @@ SMALL = {
                             q_sched=(520, 260), n_ns=32, n_users=1, n_candidates=256), [470]),
     "h_dh64_long": (Workload(name="h", n_layers=2, d_model=128, n_heads=2, ffn_hidden=256, s_len=640,
                              q_sched=(640, 320), n_ns=8, n_users=2, n_candidates=520), [640, 590]),
+    # wide models: 16 heads, and more than 16 norm-partial slots per row at d = 1024 (the GEMM
+    # epilogue loads those beyond the first 16 after its k-loop); F not a multiple of 128
+    "n_d1024_dh64": (Workload(name="n", n_layers=2, d_model=1024, n_heads=16, ffn_hidden=1088, s_len=96,
+                              q_sched=(96, 40), n_ns=3, n_users=2, n_candidates=4), [96, 50]),
+    "o_d512_dh32": (Workload(name="o", n_layers=3, d_model=512, n_heads=16, ffn_hidden=640, s_len=130,
+                             q_sched=(130, 70, 9), n_ns=6, n_users=1, n_candidates=9), [117]),
 }
 
 
@@ -92,7 +98,7 @@ def test_block_forward_matches_oracle(name):
         assert np.all(s_out[u, :npad].cpu().numpy() == 0.0)
 
 
-@pytest.mark.parametrize("name", ["a_dh32_P5", "b_dh64_P32", "c_fp8", "tiny"])
+@pytest.mark.parametrize("name", ["a_dh32_P5", "b_dh64_P32", "c_fp8", "tiny", "n_d1024_dh64"])
 def test_prefill_append_score_match_oracle(name):
     wl, lens = SMALL[name]
     print(f"case {name}", flush=True)
