@@ -67,8 +67,13 @@ def errors(got, ref):
     return max_abs, rel
 
 
-def assert_close(got, ref, wdtype: str = "bf16", what: str = ""):
+def assert_close(got, ref, wdtype: str = "bf16", what: str = "", n_layers: int = 8):
+    """The stated bars hold for models of up to 8 layers (every workload's depth). The
+    precision plan's rounding accumulates over the sublayers, so a deeper model gets the
+    max-abs bar times n_layers / 8, the relative-L2 bar unchanged (the growth with depth is
+    pinned on the CPU in test_precision_study.py)."""
     ma, rl = errors(got, ref)
     bar_ma, bar_rl = TOL[wdtype]
+    bar_ma *= max(1.0, n_layers / 8)
     print(f"    {what}: max-abs {ma:.3e} (bar {bar_ma}) rel-L2 {rl:.3e} (bar {bar_rl})", flush=True)
     assert ma <= bar_ma and rl <= bar_rl, f"{what}: max-abs {ma:.3e} rel-L2 {rl:.3e}"

@@ -45,6 +45,12 @@ SMALL = {
                               q_sched=(96, 40), n_ns=3, n_users=2, n_candidates=4), [96, 50]),
     "o_d512_dh32": (Workload(name="o", n_layers=3, d_model=512, n_heads=16, ffn_hidden=640, s_len=130,
                              q_sched=(130, 70, 9), n_ns=6, n_users=1, n_candidates=9), [117]),
+    # the largest layer count (16) and the largest NS token count (256: 256 private weight
+    # groups per GEMM, own-key ranges of 8 key blocks per candidate)
+    "p_16layers": (Workload(name="p", n_layers=16, d_model=64, n_heads=1, ffn_hidden=64, s_len=40,
+                            q_sched=tuple(range(40, 8, -2)), n_ns=2, n_users=2, n_candidates=3), [40, 7]),
+    "q_P256": (Workload(name="q", n_layers=2, d_model=64, n_heads=2, ffn_hidden=64, s_len=50,
+                        q_sched=(50, 20), n_ns=256, n_users=1, n_candidates=20), [43]),
 }
 
 
@@ -89,8 +95,8 @@ def test_block_forward_matches_oracle(name):
     s_out, ns_out = m.block_forward(*_dev(s, lens, ns))
     torch.cuda.synchronize()
     ref_t, ref_n = O.block_forward(lay, wl.q_sched, wl.n_heads, EPS, s, lens, ns)
-    assert_close(s_out.cpu().numpy(), ref_t, wl.ns_wdtype, "S tail")
-    assert_close(ns_out.cpu().numpy(), ref_n, wl.ns_wdtype, "NS out")
+    assert_close(s_out.cpu().numpy(), ref_t, wl.ns_wdtype, "S tail", wl.n_layers)
+    assert_close(ns_out.cpu().numpy(), ref_n, wl.ns_wdtype, "NS out", wl.n_layers)
     # padding rows of the S tail are exactly zero
     qL = wl.q_sched[-1]
     for u, ln in enumerate(lens):

@@ -104,3 +104,36 @@ def main() -> None:
 
 if __name__ == "__main__":
     main()
+
+
+def test_rounding_grows_with_depth():
+    """Why deeper models get a wider max-abs bar: the oracle with the GPU plan's roundings
+    (fp16 operands of the linear maps, bf16 Q / K / V) moves a 64-wide model's final rows by
+    less than the stated 3e-2 at 8 layers but by more at 16, and by less than 3e-2 * 16 / 8."""
+    from onetrans_inputs import Workload
+    wl = Workload(name="depth", n_layers=16, d_model=64, n_heads=1, ffn_hidden=64, s_len=40,
+                  q_sched=tuple(range(40, 8, -2)), n_ns=2, n_users=2, n_candidates=3)
+    lens = np.array([40, 7], np.int32)
+    f16, b16 = FORMATS["fp16"], FORMATS["bf16"]
+    rms, gelu, att = OO.rmsnorm, OO.gelu, OO.attend
+
+    def final_rows(L, emulate):
+        w = wl.with_(n_layers=L, q_sched=wl.q_sched[:L])
+        s, _ = make_s_tokens(w)
+        for u in range(s.shape[0]):
+            s[u, : w.s_len - lens[u]] = 0.0
+        try:
+            if emulate:
+                OO.rmsnorm = lambda x, g, eps: f16(rms(x, g, eps))
+                OO.gelu = lambda x: f16(gelu(x))
+                OO.attend = lambda q, k, v, vis, h: att(b16(q), b16(k), b16(v), vis, h)
+            t, n = O.block_forward(O.layers_from_arrays(make_weights(w)), w.q_sched, w.n_heads, 1e-6, s, lens,
+                                   make_ns_tokens(w))
+        finally:
+            OO.rmsnorm, OO.gelu, OO.attend = rms, gelu, att
+        return np.concatenate([t.ravel(), n.ravel()])
+
+    dev = {L: float(np.abs(final_rows(L, True) - final_rows(L, False)).max()) for L in (8, 16)}
+    print("max-abs moved by the emulated roundings:", dev)
+    assert dev[8] < 3e-2 < dev[16] < 3e-2 * 16 / 8
+
