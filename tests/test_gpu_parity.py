@@ -458,6 +458,40 @@ def test_zero_candidates_and_capacity_errors():
         mdl.score_candidates(cache, 2, nd[0])
 
 
+def test_append_fills_cache_to_capacity():
+    # append_cap = 56 with 200 input rows at layers 0 and 1: their caches hold exactly 256
+    # keys (four 64-key tiles, no rounding slack), and two appends (40 + 16 events) fill them
+    # to the last slot; outputs and scoring against the full cache match the oracle, and
+    # one event more is refused without touching the cache
+    from unified_transformer_recommender_onetrans_amd import OneTransError
+    wl, lens = SMALL["b_dh64_P32"]
+    print("case b_dh64_P32, append_cap 56", flush=True)
+    mdl, lay = model(wl, append_cap=56)
+    s, lens, ns = _inputs(wl, lens)
+    sd, ld, nd = _dev(s, lens, ns)
+    B = s.shape[0]
+    cache = mdl.new_cache(B)
+    mdl.user_prefill(sd, ld, cache)
+    new1 = make_append_tokens(wl, m=40)
+    new2 = make_append_tokens(wl, seed=1, m=16)
+    out1 = mdl.kv_append(bf16_dev(new1), cache)
+    out2 = mdl.kv_append(bf16_dev(new2), cache)
+    assert cache.n_appended == 56
+    with pytest.raises(OneTransError):
+        mdl.kv_append(bf16_dev(make_append_tokens(wl, seed=2, m=1)), cache)
+    assert cache.n_appended == 56
+    scores = [mdl.score_candidates(cache, u, nd[u]) for u in range(B)]
+    torch.cuda.synchronize()
+    for u in range(B):
+        oc, _ = O.prefill(lay, wl.q_sched, wl.n_heads, EPS, s[u], int(lens[u]))
+        oc, o1 = O.append(lay, wl.n_heads, EPS, oc, new1[u])
+        oc, o2 = O.append(lay, wl.n_heads, EPS, oc, new2[u])
+        assert_close(out1[u].cpu().numpy(), o1, wl.ns_wdtype, f"user {u} append 1")
+        assert_close(out2[u].cpu().numpy(), o2, wl.ns_wdtype, f"user {u} append 2")
+        assert_close(scores[u].cpu().numpy(), O.score(lay, wl.n_heads, EPS, oc, ns[u]), wl.ns_wdtype,
+                     f"user {u} score against the full cache")
+
+
 # ---------------------------------------------------------------------------
 # invariants on the GPU
 # ---------------------------------------------------------------------------
