@@ -96,6 +96,51 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&s
   st.l += ps;
 }
 
+// 32 row-major keys [t0, t0 + 32) of a K / V block (rows past n_rows - 1 are read as that
+// row and masked) into the online-softmax state st of this lane's query, for the keys
+// where vis(key) holds: the NS rows' own keys and the user's cached NS rows. The V operand
+// rows load right after the score MFMAs are issued, so their latency runs under the mask
+// and the exponentials rather than after them; the mask is a select per score.
+// Register j of the scores holds key t0 + 8*(j/4) + 4*(lane/32) + j%4 (rows in order), so
+// the 8 probabilities of P.V operand c are keys t0 + 16c + 4*(lane/32) + {0..3, 8..11}.
+template <int DH, class Vis>
+__device__ __forceinline__ void own_key_block(Softmax<DH>& st, const bf16x8 (&qf)[DH / 16], const __bf16* knb,
+                                              const __bf16* vnb, int n_rows, int t0, bool q_ok, float scale_log2,
+                                              Vis vis) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int krow = min(t0 + l32, n_rows - 1);
+  f32x16 sk[1];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sk[0][j] = 0.f;
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s) {
+    const bf16x8 a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
+    sk[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sk[0], 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int key = t0 + 8 * (j >> 2) + half * 4 + (j & 3);
+    sk[0][j] = (q_ok & vis(key)) ? sk[0][j] : -INFINITY;
+  }
+  bf16x8 pk[1][2];
+  softmax_update<DH, 1>(st, sk, pk, scale_log2);
+  bf16x8 va[2][DH / 32];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), n_rows - 1);
+        va[c][db][i] = vnb[(long)key * DH + db * 32 + l32];
+      }
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c][db], pk[0][c], st.o[db], 0, 0, 0);
+}
+
 // Pieces of one 64-key tile against a wave's 32 queries. sb holds the tile: K rows
 // (XOR-swizzled 16-byte chunks) followed by V^T rows of 64 keys (128 bytes each).
 //
@@ -694,37 +739,8 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   OutRow<DH> orow;
   if (kh == 0 && q_ok) out_row_load<DH, false>(p, seg, h, qi, orow);
   if (kh == 0 && wave_live) {
-    // 32 keys [t0, t0 + 32) of a row-major K / V block (rows past n_rows - 1 are read as
-    // that row and masked), visible to this lane when vis(key) holds
     auto key_block = [&](const __bf16* knb, const __bf16* vnb, int n_rows, int t0, auto vis) {
-      f32x16 sk[1];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sk[0][j] = 0.f;
-      const int krow = min(t0 + l32, n_rows - 1);
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s) {
-        const bf16x8 a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
-        sk[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sk[0], 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = t0 + 8 * (j >> 2) + half * 4 + (j & 3);
-        if (!(q_ok && vis(key))) sk[0][j] = -INFINITY;
-      }
-      bf16x8 pk[1][2];
-      softmax_update<DH, 1>(st, sk, pk, p.scale_log2);
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int db = 0; db < DH / 32; ++db) {
-          bf16x8 a;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), n_rows - 1);
-            a[i] = vnb[(long)key * DH + db * 32 + l32];
-          }
-          st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][c], st.o[db], 0, 0, 0);
-        }
+      own_key_block<DH>(st, qf, knb, vnb, n_rows, t0, q_ok, p.scale_log2, vis);
     };
     // the user's cached NS rows: earlier NS positions, seen in full by every query
     if (p.n_x > 0) {
@@ -743,7 +759,7 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
 #pragma unroll 1
     for (int t0 = g_lo; t0 <= g_hi; t0 += 32)
       key_block(p.kn + seg * p.kn_seg_stride + h * p.kn_head_stride, p.vn + seg * p.kn_seg_stride + h * p.kn_head_stride,
-                p.nq, t0, [&](int key) { return key <= qi && key >= my_first; });
+                p.nq, t0, [&](int key) { return (key <= qi) & (key >= my_first); });
   }
 
   // ---- merge the two key halves of each query block (LDS of the tile ring is free) ----
@@ -928,34 +944,7 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db) st2.o[db] = o[db];
     auto key_block = [&](const __bf16* knb, const __bf16* vnb, int n_rows, int t0, auto vis) {
-      f32x16 sk[1];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sk[0][j] = 0.f;
-      const int krow = min(t0 + l32, n_rows - 1);
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s) {
-        const bf16x8 a = *(const bf16x8*)(knb + (long)krow * DH + s * 16 + half * 8);
-        sk[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sk[0], 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = t0 + 8 * (j >> 2) + half * 4 + (j & 3);
-        if (!(q_ok && vis(key))) sk[0][j] = -INFINITY;
-      }
-      bf16x8 pk[1][2];
-      softmax_update<DH, 1>(st2, sk, pk, p.scale_log2);
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int db = 0; db < DH / 32; ++db) {
-          bf16x8 a;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int key = min(t0 + 16 * c + half * 4 + (i & 3) + 8 * (i >> 2), n_rows - 1);
-            a[i] = vnb[(long)key * DH + db * 32 + l32];
-          }
-          st2.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][c], st2.o[db], 0, 0, 0);
-        }
+      own_key_block<DH>(st2, qf, knb, vnb, n_rows, t0, q_ok, p.scale_log2, vis);
     };
     if (p.n_x > 0) {
       const __bf16* xkb = p.xk + h * p.x_head_stride;
@@ -972,7 +961,7 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
 #pragma unroll 1
     for (int t0 = g_lo; t0 <= g_hi; t0 += 32)
       key_block(p.kn + seg * p.kn_seg_stride + h * p.kn_head_stride, p.vn + seg * p.kn_seg_stride + h * p.kn_head_stride,
-                p.nq, t0, [&](int key) { return key <= qi && key >= my_first; });
+                p.nq, t0, [&](int key) { return (key <= qi) & (key >= my_first); });
     l_all = st2.l + __shfl_xor(st2.l, 32);
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db) o[db] = st2.o[db];
