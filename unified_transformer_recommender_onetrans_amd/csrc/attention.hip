@@ -811,7 +811,10 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "tile split");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a wave-uniform value: the tile offsets and ring addresses derived
+  // from it go to the buffer DMA's scalar operands (a per-lane value there makes the
+  // compiler loop over its distinct values around every DMA instruction)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   // (query block, head, segment). GROUPED: a 1-D grid numbered so that each XCD holds a
   // contiguous range of them (the hardware deals workgroup L to XCD L % 8): the query
