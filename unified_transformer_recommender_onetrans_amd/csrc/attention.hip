@@ -411,9 +411,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
 
   const int t_first = (key_lo / KT) * KT;
   const int ntiles = key_hi > t_first ? (key_hi - t_first + KT - 1) / KT : 0;
+  // The first STAGES - 1 tiles issue whatever ntiles is (past the cached keys they read
+  // zeros into slots the loop never reads): with a fixed count the compiler waits for the
+  // query loads above without waiting for this burst. The waits below count them, and the
+  // one after the loop keeps a wave from ending while a DMA still writes this LDS.
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ntiles) issue(t_first + s * KT, s);
+  for (int s = 0; s < STAGES - 1; ++s) issue(t_first + s * KT, s);
 
 #pragma unroll 1
   for (int it = 0; it < ntiles; ++it) {
@@ -427,6 +430,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
                     p.scale_log2);
     }
   }
+  wait_vmcnt<0>();
 
   const float l_tot = st.l + __shfl_xor(st.l, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -564,11 +568,16 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
     for (int s = 0; s < DH / 16; ++s)
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sb + k_frag[s]), qf[s], sc, 0, 0, 0);
   };
-  if (ntiles > 0) issue_k(0, 0);
-  if (ntiles > 1) issue_k(1, 1);
-  if (ntiles > 0) issue_v(0, 0);
-  if (ntiles > 2) issue_k(2, 2);
-  if (ntiles > 1) issue_v(1, 1);
+  // The first five issue whatever ntiles is: a tile past the cached keys reads zeros
+  // (buffer bounds) into ring slots the key loop never reads, and a fixed count lets the
+  // compiler wait for the query loads above without waiting for this burst (behind a
+  // conditional issue it cannot count the loads in flight and waits for all of them).
+  // Every wait below counts these five, so a shorter walk only waits for more of them.
+  issue_k(0, 0);
+  issue_k(1, 1);
+  issue_v(0, 0);
+  issue_k(2, 2);
+  issue_v(1, 1);
 
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -600,10 +609,8 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
   };
   f32x16 sc;
   if (ntiles > 0) {
-    // only K(0) is needed here: leave the loads issued after it in flight
-    if (ntiles > 2) wait_vmcnt<2 * PER_TILE>();        // K(1), V(0), K(2), V(1)
-    else if (ntiles == 2) wait_vmcnt<K_INSTR + 2 * V_INSTR>();  // K(1), V(0), V(1)
-    else wait_vmcnt<V_INSTR>();                         // V(0)
+    // only K(0) is needed here: leave K(1), V(0), K(2), V(1) in flight
+    wait_vmcnt<2 * PER_TILE>();
     lds_barrier();
     scores(0, sc);
   }
@@ -764,7 +771,10 @@ __global__ __launch_bounds__(NB * 128) void attn_ns2_kernel(AttnParams p) {
 
   // ---- merge the two key halves of each query block (LDS of the tile ring is free) ----
   const float l_half = st.l + __shfl_xor(st.l, 32);
-  __syncthreads();  // every wave is past its last tile read
+  // no DMA of this wave is still writing the ring (with no cached key to walk, the first
+  // five were never waited for) and every wave is past its last tile read
+  wait_vmcnt<0>();
+  __syncthreads();
   float* mw = (float*)(smem + qb * MERGE);
   if (kh == 1) {
     mw[lane] = st.m;
