@@ -847,19 +847,6 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   const int qi = wq0 + l32;
   const bool q_ok = qi < p.nq;
 
-  bf16x8 qf[DH / 16];
-  {
-    const __bf16* qrow = p.q + seg * p.q_seg_stride + h * p.q_head_stride + (long)(q_ok ? qi : 0) * DH;
-#pragma unroll
-    for (int s = 0; s < DH / 16; ++s) {
-      bf16x8 v = *(const bf16x8*)(qrow + s * 16 + half * 8);
-      if (!q_ok) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.f;
-      }
-      qf[s] = v;
-    }
-  }
   const int vf = p.valid_from[seg];
   const int key_lo = max(0, vf - p.key_pos0);
   const int qlast = min(wq0 + 31, p.nq - 1);
@@ -878,8 +865,6 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   const int t_first = (key_lo / KT) * KT;
   const int ntiles = key_hi > t_first ? (key_hi - t_first + KT - 1) / KT : 0;
   const int n_my = wave < ntiles ? (ntiles - wave + KS - 1) / KS : 0;
-  OutRow<DH> orow;  // wave 0 writes the merged rows
-  if (wave == 0 && q_ok) out_row_load<DH, true>(p, seg, h, qi, orow);
   const __amdgpu_buffer_rsrc_t krs =
       buffer_rsrc(p.k + seg * p.kv_seg_stride + h * p.kv_head_stride, (uint32_t)p.kv_cap * KROW);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -901,7 +886,26 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
                 (uint32_t)t0 * 2, (lds_void*)(sb + K_BYTES + i * 1024));
     }
   };
-  if (n_my > 0) issue(0);
+  // The first tile issues before the query and output-row loads, and whatever n_my is (a
+  // wave with no tile reads zeros or unused keys into its own ring, waited for before the
+  // merge reuses the LDS): behind loads still in flight, or a conditional issue, the
+  // compiler made it wait for all of them first.
+  issue(0);
+  bf16x8 qf[DH / 16];
+  {
+    const __bf16* qrow = p.q + seg * p.q_seg_stride + h * p.q_head_stride + (long)(q_ok ? qi : 0) * DH;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+      bf16x8 v = *(const bf16x8*)(qrow + s * 16 + half * 8);
+      if (!q_ok) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.f;
+      }
+      qf[s] = v;
+    }
+  }
+  OutRow<DH> orow;  // wave 0 writes the merged rows
+  if (wave == 0 && q_ok) out_row_load<DH, true>(p, seg, h, qi, orow);
 #pragma unroll 1
   for (int j = 0; j < n_my; ++j) {
     if (j + 1 < n_my) {
@@ -916,6 +920,7 @@ __global__ __launch_bounds__(KS * 64) void attn_split_kernel(AttnParams p) {
   }
 
   // ---- merge: every wave's lane l holds the same query and O layout ----
+  wait_vmcnt<0>();  // a wave without tiles has not waited for its first DMA yet
   __syncthreads();  // all rings are done; reuse the LDS for the partial results
   float* mw = (float*)(smem + wave * MERGE);
   mw[lane] = st.m;
