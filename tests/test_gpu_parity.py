@@ -51,6 +51,10 @@ SMALL = {
                             q_sched=tuple(range(40, 8, -2)), n_ns=2, n_users=2, n_candidates=3), [40, 7]),
     "q_P256": (Workload(name="q", n_layers=2, d_model=64, n_heads=2, ffn_hidden=64, s_len=50,
                         q_sched=(50, 20), n_ns=256, n_users=1, n_candidates=20), [43]),
+    # a history of 10000 events (the pages speak of behaviour sequences beyond 10000 steps)
+    # in 10240 slots: 160 key tiles per query block in the first layer
+    "r_long10k": (Workload(name="r", n_layers=2, d_model=64, n_heads=2, ffn_hidden=128, s_len=10240,
+                           q_sched=(10240, 100), n_ns=4, n_users=1, n_candidates=6), [10000]),
 }
 
 
