@@ -98,9 +98,9 @@ __device__ __forceinline__ void softmax_update(Softmax<DH>& st, const f32x16 (&s
 
 // 32 row-major keys [t0, t0 + 32) of a K / V block (rows past n_rows - 1 are read as that
 // row and masked) into the online-softmax state st of this lane's query, for the keys
-// where vis(key) holds: the NS rows' own keys and the user's cached NS rows. The V operand
-// rows load right after the score MFMAs are issued, so their latency runs under the mask
-// and the exponentials rather than after them; the mask is a select per score.
+// where vis(key) holds: the NS rows' own keys and the user's cached NS rows. The mask is a
+// select per score. The V operand rows load after the exponentials: loaded with the K rows
+// they would be held across the softmax, which raises the register count of the callers.
 // Register j of the scores holds key t0 + 8*(j/4) + 4*(lane/32) + j%4 (rows in order), so
 // the 8 probabilities of P.V operand c are keys t0 + 16c + 4*(lane/32) + {0..3, 8..11}.
 template <int DH, class Vis>
